@@ -1,0 +1,330 @@
+// Host side of libmsa: argument validation, route choice, split-K sizing,
+// workspace carving and kernel launches on the caller's stream.
+//
+// Routes follow the "msa" page of the MAX Mojo docs (routes paragraph): the
+// maximum number of new tokens of any sequence picks the kernels -- 1 is a
+// decode step, 2..8 a speculative-decode step, more a prefill step -- and
+// every route takes the same arguments.  Grid sizes derive from host bounds
+// only, never from device data, so launches are graph-capturable.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "msa.h"
+#include "msa_kernels.h"
+
+namespace {
+
+using namespace msa;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxPartitions = 64;
+constexpr int kMaxDevices = 64;
+constexpr size_t kMaxLds = 64 * 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Per-device facts read once: compute-unit count and whether it is gfx950.
+std::atomic<int> g_dev_cus[kMaxDevices];
+std::atomic<int> g_dev_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+int current_device(int* cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_DEVICE;
+  int ok = g_dev_ok[dev].load();
+  if (ok == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MSA_ERR_DEVICE;
+    ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_cus[dev].store(prop.multiProcessorCount);
+    g_dev_ok[dev].store(ok);
+  }
+  if (ok != 1) return MSA_ERR_DEVICE;
+  if (cus) *cus = g_dev_cus[dev].load();
+  return MSA_OK;
+}
+
+enum class Route { Decode, Spec, Prefill };
+
+Route route_of(const msa_ragged& rg) {
+  if (rg.max_seq_length <= 1) return Route::Decode;
+  if (rg.max_seq_length <= MSA_MAX_SPEC_DRAFT) return Route::Spec;
+  return Route::Prefill;
+}
+
+// Blocks the longest possible sequence may hold.
+int64_t max_blocks(const msa_ragged& rg) {
+  return ((int64_t)rg.max_cache_length + rg.max_seq_length + MSA_BLOCK_SIZE - 1) / MSA_BLOCK_SIZE;
+}
+
+int64_t row_capacity(const msa_ragged& rg) { return (int64_t)rg.batch * rg.max_seq_length; }
+
+int check_ragged(const msa_ragged* rg) {
+  if (!rg) return MSA_ERR_NULL;
+  if (rg->batch < 0 || rg->max_seq_length < 0 || rg->max_cache_length < 0) return MSA_ERR_PARAM;
+  if (rg->batch == 0 || rg->max_seq_length == 0) return MSA_OK;
+  if (!rg->input_row_offsets || !rg->cache_lengths || !rg->kv_lookup_table) return MSA_ERR_NULL;
+  if (rg->lookup_stride < 1) return MSA_ERR_SHAPE;
+  if (max_blocks(*rg) > MSA_MAX_BLOCKS) return MSA_ERR_SHAPE;
+  if (row_capacity(*rg) > (int64_t)INT32_MAX / 8) return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+bool empty_batch(const msa_ragged& rg) { return rg.batch == 0 || rg.max_seq_length == 0; }
+
+int check_cache(const msa_paged_cache* c, bool allow_fp8) {
+  if (!c) return MSA_ERR_NULL;
+  if (!c->data) return MSA_ERR_NULL;
+  if (c->dtype != MSA_DTYPE_BF16 && c->dtype != MSA_DTYPE_FP8_E4M3) return MSA_ERR_DTYPE;
+  if (c->dtype == MSA_DTYPE_FP8_E4M3 && !allow_fp8) return MSA_ERR_DTYPE;
+  if (c->page_size != MSA_BLOCK_SIZE || c->head_dim != MSA_HEAD_DIM) return MSA_ERR_SHAPE;
+  if (c->num_pages < 1 || c->num_heads < 1) return MSA_ERR_SHAPE;
+  const int64_t esz = c->dtype == MSA_DTYPE_BF16 ? 2 : 1;
+  if (reinterpret_cast<uintptr_t>(c->data) % 16) return MSA_ERR_SHAPE;
+  for (int64_t st : {c->page_stride, c->head_stride, c->token_stride})
+    if (st < 0 || (st * esz) % 16) return MSA_ERR_SHAPE;
+  if (c->token_stride < MSA_HEAD_DIM) return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+Pool pool_of(const msa_paged_cache& c) {
+  return Pool{c.data, c.page_stride, c.head_stride, c.token_stride, c.num_pages};
+}
+
+Ragged ragged_of(const msa_ragged& rg) {
+  return Ragged{rg.input_row_offsets, rg.cache_lengths, rg.kv_lookup_table, rg.lookup_stride,
+                rg.batch, rg.max_seq_length};
+}
+
+int check_selection(int32_t top_k, int32_t init_blocks, int32_t local_blocks) {
+  if (top_k < 1 || top_k > MSA_MAX_TOPK) return MSA_ERR_PARAM;
+  if (init_blocks < 0 || local_blocks < 0) return MSA_ERR_PARAM;
+  if ((int64_t)init_blocks + local_blocks > top_k) return MSA_ERR_PARAM;
+  return MSA_OK;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// ---- indexer ---------------------------------------------------------------
+
+size_t indexer_ws(const msa_ragged& rg, int32_t num_kv_heads, int32_t top_k) {
+  if (empty_batch(rg)) return 0;
+  const int64_t nb = max_blocks(rg);
+  if (nb <= top_k) return 0;     // every row selects all of its blocks
+  return align_up((size_t)row_capacity(rg) * num_kv_heads * nb * sizeof(float));
+}
+
+// ---- attention ---------------------------------------------------------------
+
+struct AttnPlan {
+  int tpw, ntg, np;
+};
+
+AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int req_np, int cus) {
+  AttnPlan pl{};
+  const Route r = route_of(rg);
+  pl.tpw = r == Route::Decode ? 1 : std::min(16 / G, std::max(1, rg.max_seq_length));
+  if (r == Route::Prefill) pl.tpw = 16 / G;
+  const int ntok_groups = (rg.max_seq_length + pl.tpw - 1) / pl.tpw;
+  pl.ntg = std::min(4, ntok_groups);
+  if (r == Route::Prefill) {
+    pl.np = 1;
+    return pl;
+  }
+  if (req_np > 0) {
+    pl.np = req_np;
+    return pl;
+  }
+  // CU fill: aim for about 8 resident waves per CU; keep at least two blocks
+  // per partition when the batch alone already gives a few waves per CU.
+  const int64_t base = (int64_t)rg.batch * H_kv * ntok_groups;
+  const int64_t target = (int64_t)cus * 8;
+  int64_t np = (target + base - 1) / std::max<int64_t>(1, base);
+  const int union_blocks = std::min<int64_t>(top_k * pl.tpw, max_blocks(rg));
+  const int min_per = base >= cus / 2 ? 2 : 1;
+  np = std::min<int64_t>(np, std::max(1, union_blocks / min_per));
+  pl.np = (int)std::max<int64_t>(1, std::min<int64_t>(np, kMaxPartitions));
+  return pl;
+}
+
+size_t attention_ws(const msa_ragged& rg, int H_q, int np) {
+  if (empty_batch(rg) || np <= 1) return 0;
+  const size_t rows = (size_t)np * row_capacity(rg) * H_q;
+  return align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads) return MSA_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_NULL: return "null pointer";
+    case MSA_ERR_SHAPE: return "unsupported shape, stride or alignment";
+    case MSA_ERR_PARAM: return "parameter out of range";
+    case MSA_ERR_DTYPE: return "unsupported storage type";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_LAUNCH: return "kernel launch failed";
+    case MSA_ERR_DEVICE: return "no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+size_t msa_indexer_workspace_bytes(const msa_ragged* rg, int32_t num_kv_heads, int32_t top_k) {
+  if (check_ragged(rg) != MSA_OK || num_kv_heads < 1 || top_k < 1) return 0;
+  return indexer_ws(*rg, num_kv_heads, top_k);
+}
+
+int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cache* index_k,
+                      const msa_ragged* rg, int32_t num_kv_heads, int32_t top_k,
+                      int32_t init_blocks, int32_t local_blocks, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_ragged(rg);
+  if (st != MSA_OK) return st;
+  if ((st = check_selection(top_k, init_blocks, local_blocks)) != MSA_OK) return st;
+  if (num_kv_heads < 1) return MSA_ERR_SHAPE;
+  if ((st = check_cache(index_k, false)) != MSA_OK) return st;
+  if (index_k->num_heads != 1 && index_k->num_heads != num_kv_heads) return MSA_ERR_SHAPE;
+  if (!d_indices || !q_idx) return MSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(d_indices)) return MSA_ERR_SHAPE;
+  if (empty_batch(*rg)) return MSA_OK;
+  const size_t need = indexer_ws(*rg, num_kv_heads, top_k);
+  if (need && !workspace) return MSA_ERR_NULL;
+  if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if ((st = current_device(nullptr)) != MSA_OK) return st;
+
+  IndexerParams p{};
+  p.q_idx = static_cast<const uint16_t*>(q_idx);
+  p.ik = pool_of(*index_k);
+  p.rg = ragged_of(*rg);
+  p.scores = static_cast<float*>(workspace);
+  p.d_indices = d_indices;
+  p.nbmax = (int32_t)max_blocks(*rg);
+  p.H_kv = num_kv_heads;
+  p.H_ik = index_k->num_heads;
+  p.top_k = top_k;
+  p.init = init_blocks;
+  p.local = local_blocks;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.nbmax > top_k) {
+    if (launch_indexer_decode(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  }
+  if (launch_topk(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  return MSA_OK;
+}
+
+int msa_attention_partitions(const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t top_k, int32_t num_partitions) {
+  int st = check_ragged(rg);
+  if (st != MSA_OK) return st;
+  if ((st = check_heads(num_q_heads, num_kv_heads)) != MSA_OK) return st;
+  if (top_k < 1 || top_k > MSA_MAX_TOPK) return MSA_ERR_PARAM;
+  if (num_partitions < 0 || num_partitions > kMaxPartitions) return MSA_ERR_PARAM;
+  if (empty_batch(*rg)) return 1;
+  int cus = 256;
+  if (num_partitions == 0 && current_device(&cus) != MSA_OK) cus = 256;
+  return plan_attention(*rg, num_q_heads / num_kv_heads, num_kv_heads, top_k, num_partitions, cus).np;
+}
+
+size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t top_k, int32_t num_partitions) {
+  const int np = msa_attention_partitions(rg, num_q_heads, num_kv_heads, top_k, num_partitions);
+  if (np < 1) return 0;
+  return attention_ws(*rg, num_q_heads, np);
+}
+
+int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
+                        const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                        const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t top_k, float scale, int32_t num_partitions, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check_ragged(rg);
+  if (st != MSA_OK) return st;
+  if ((st = check_heads(num_q_heads, num_kv_heads)) != MSA_OK) return st;
+  if (top_k < 1 || top_k > MSA_MAX_TOPK) return MSA_ERR_PARAM;
+  if (num_partitions < 0 || num_partitions > kMaxPartitions) return MSA_ERR_PARAM;
+  if (!(scale == scale)) return MSA_ERR_PARAM;
+  if ((st = check_cache(k_cache, true)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, true)) != MSA_OK) return st;
+  if (k_cache->dtype != v_cache->dtype) return MSA_ERR_DTYPE;
+  if (k_cache->num_heads != num_kv_heads || v_cache->num_heads != num_kv_heads) return MSA_ERR_SHAPE;
+  if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_SHAPE;
+  if (!output || !q || !d_indices) return MSA_ERR_NULL;
+  if (!aligned16(output) || !aligned16(q) || !aligned16(d_indices)) return MSA_ERR_SHAPE;
+  if (empty_batch(*rg)) return MSA_OK;
+  // The automatic partition count depends on the device's CU count; an
+  // explicit one does not, so its workspace is checked before any device query.
+  int cus = 0;
+  if (num_partitions == 0 && (st = current_device(&cus)) != MSA_OK) return st;
+  const int G = num_q_heads / num_kv_heads;
+  const AttnPlan pl = plan_attention(*rg, G, num_kv_heads, top_k, num_partitions, cus);
+  const size_t need = attention_ws(*rg, num_q_heads, pl.np);
+  if (need && !workspace) return MSA_ERR_NULL;
+  if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (num_partitions != 0 && (st = current_device(nullptr)) != MSA_OK) return st;
+
+  AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.d_indices = d_indices;
+  p.k = pool_of(*k_cache);
+  p.v = pool_of(*v_cache);
+  p.rg = ragged_of(*rg);
+  p.H_q = num_q_heads;
+  p.H_kv = num_kv_heads;
+  p.G = G;
+  p.top_k = top_k;
+  p.tpw = pl.tpw;
+  p.ntg = pl.ntg;
+  p.np = pl.np;
+  p.rcap = (int32_t)row_capacity(*rg);
+  p.nbmax = (int32_t)max_blocks(*rg);
+  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  p.out = static_cast<uint16_t*>(output);
+  if (pl.np > 1) {
+    const size_t rows = (size_t)pl.np * p.rcap * num_q_heads;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align_up(rows * MSA_HEAD_DIM * sizeof(float)));
+  }
+  if (attention_decode_lds_bytes(p) > kMaxLds) return MSA_ERR_PARAM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_attention_decode(p, k_cache->dtype == MSA_DTYPE_FP8_E4M3, s) != hipSuccess)
+    return MSA_ERR_LAUNCH;
+  if (pl.np > 1) {
+    CombineParams c{p.part_o, p.part_lse, rg->input_row_offsets, p.out, rg->batch,
+                    rg->max_seq_length, pl.np, num_q_heads, p.rcap};
+    if (launch_combine(c, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
+int msa_splitk_combine(void* output, const float* partial_o, const float* partial_lse,
+                       const int32_t* input_row_offsets, int32_t batch, int32_t max_seq_length,
+                       int32_t num_partitions, int32_t num_q_heads, void* stream) {
+  if (batch < 0 || max_seq_length < 0 || num_partitions < 1 || num_partitions > kMaxPartitions ||
+      num_q_heads < 1)
+    return MSA_ERR_PARAM;
+  if (batch == 0 || max_seq_length == 0) return MSA_OK;
+  if (!output || !partial_o || !partial_lse || !input_row_offsets) return MSA_ERR_NULL;
+  if (!aligned16(output) || !aligned16(partial_o)) return MSA_ERR_SHAPE;
+  if ((int64_t)batch * max_seq_length > (int64_t)INT32_MAX / 8) return MSA_ERR_SHAPE;
+  const int st = current_device(nullptr);
+  if (st != MSA_OK) return st;
+  CombineParams c{partial_o, partial_lse, input_row_offsets, static_cast<uint16_t*>(output), batch,
+                  max_seq_length, num_partitions, num_q_heads, batch * max_seq_length};
+  if (launch_combine(c, static_cast<hipStream_t>(stream)) != hipSuccess) return MSA_ERR_LAUNCH;
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,335 @@
+// Sparse attention over selected KV blocks (decode / speculative decode
+// route) with split-K partitions, and the split-K combine.
+//
+// Semantics ("ferrox_core::block_sparse" page, positions_of_blocks and the
+// masked pass it feeds; "msa" page, speculative-decode route): token t of
+// sequence b sits at position p = cache_lengths[b] + t and attends to the
+// positions j <= p of the blocks its KV head selected, with an ordinary
+// softmax; every query head of the GQA group reads the same blocks.
+//
+// Work item = (sequence, KV head, group of `tpw` tokens, partition).  One
+// wave owns an item.  Its MFMA columns are (token, query head) pairs:
+// 16 = tpw * G (decode uses one token, so with G = 8 half the columns idle).
+// The wave builds the ascending union of its tokens' block lists in LDS
+// (with a per-block membership mask), takes its partition's slice of it,
+// and streams each block's K and V tiles straight from HBM into MFMA
+// operand registers:
+//   S^T = K Q^T        A = K rows (positions), B = Q^T  -> C[position][column]
+//   O^T += V^T P^T     A = V^T built in registers by 16-bit permutes,
+//                      B = P^T, which is exactly the C layout of S^T
+// so the softmax statistics of a column stay in the lanes that own it and
+// no LDS round trip is needed.  Online softmax runs per 64-position half
+// block in log2 units.
+#include "msa_common.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int ntok_groups = (p.rg.max_seq + p.tpw - 1) / p.tpw;
+  const int ntgb = (ntok_groups + W - 1) / W;
+  int x = blockIdx.x;
+  const int pi = x % p.np;
+  x /= p.np;
+  const int tgb = x % ntgb;
+  x /= ntgb;
+  const int h = x % p.H_kv;
+  const int b = x / p.H_kv;
+
+  const int r0 = p.rg.offs[b];
+  const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);   // keeps rows < rcap
+  const int c = p.rg.clen[b];
+  const int tok0 = (tgb * W + wave) * p.tpw;
+  const int ntok = max(0, min(n - tok0, p.tpw));
+
+  // ---- union of the wave's token selections, ascending, in LDS ----------
+  const int nbw = (p.nbmax + 31) >> 5;
+  const int cap = p.tpw * p.top_k;
+  uint32_t* bm = lds + wave * (p.tpw * nbw + 2 * cap);
+  int32_t* uid = reinterpret_cast<int32_t*>(bm + p.tpw * nbw);
+  uint32_t* umk = reinterpret_cast<uint32_t*>(uid + cap);
+  for (int i = lane; i < p.tpw * nbw; i += 64) bm[i] = 0u;
+  __syncthreads();
+  for (int tl = 0; tl < ntok; ++tl) {
+    const int tok = tok0 + tl;
+    const int nbt = min((c + tok) / kBlock + 1, p.nbmax);
+    const int32_t* lst = p.d_indices + ((size_t)(r0 + tok) * p.H_kv + h) * p.top_k;
+    for (int i = lane; i < p.top_k; i += 64) {
+      const int id = lst[i];
+      if (id >= 0 && id < nbt) atomicOr(&bm[tl * nbw + (id >> 5)], 1u << (id & 31));
+    }
+  }
+  __syncthreads();
+  int nU = 0;
+  for (int w0 = 0; w0 < nbw; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t u = 0u;
+    if (w < nbw)
+      for (int tl = 0; tl < ntok; ++tl) u |= bm[tl * nbw + w];
+    const int cnt = __popc(u);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int pos = nU + incl - cnt;
+    while (u) {
+      const int bit = __ffs(u) - 1;
+      u &= u - 1u;
+      uint32_t mk = 0u;
+      for (int tl = 0; tl < ntok; ++tl) mk |= ((bm[tl * nbw + w] >> bit) & 1u) << tl;
+      uid[pos] = w * 32 + bit;
+      umk[pos] = mk;
+      ++pos;
+    }
+    nU += __shfl(incl, 63);
+  }
+  __syncthreads();
+
+  // ---- this partition's slice of the union --------------------------------
+  const int per = (nU + p.np - 1) / p.np;
+  const int e_lo = min(nU, pi * per);
+  const int e_hi = min(nU, e_lo + per);
+
+  // ---- columns: (token, query head) pairs ---------------------------------
+  const int tl_col = l16 / p.G;
+  const int g_col = l16 % p.G;
+  const bool col_ok = tl_col < ntok;
+  const int p_col = c + tok0 + tl_col;
+  const int qrow = r0 + tok0 + tl_col;
+  const int hq = h * p.G + g_col;
+  const int p_max = c + tok0 + ntok - 1;
+
+  u32x4 qf[4];
+  {
+    const uint16_t* qp = p.q + ((size_t)qrow * p.H_q + hq) * kDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int d0 = FP8 ? 32 * g + 8 * s : 32 * s + 8 * g;
+      qf[s] = col_ok ? ld16(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4 O[8];
+#pragma unroll
+  for (int T = 0; T < 8; ++T) O[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = neg_inf(), l_run = 0.f;
+
+  const int esz = FP8 ? 1 : 2;
+  const char* kpool = static_cast<const char*>(p.k.data);
+  const char* vpool = static_cast<const char*>(p.v.data);
+  const size_t kts = (size_t)p.k.token_stride * esz, vts = (size_t)p.v.token_stride * esz;
+
+  for (int e = e_lo; e < e_hi; ++e) {
+    const int blk = uniform(uid[e]);
+    const uint32_t msk = uniform(umk[e]);
+    const int page = uniform(p.rg.table[(size_t)b * p.rg.stride + blk]);
+    if ((unsigned)page >= (unsigned)p.k.num_pages) continue;
+    const int plim = (col_ok && ((msk >> tl_col) & 1u)) ? p_col : -1;
+    const char* kb = kpool + ((size_t)page * p.k.page_stride + (size_t)h * p.k.head_stride) * esz;
+    const char* vb = vpool + ((size_t)page * p.v.page_stride + (size_t)h * p.v.head_stride) * esz;
+
+#pragma unroll 1
+    for (int hb = 0; hb < 2; ++hb) {
+      const int rb = 64 * hb;
+      const int pos0 = blk * kBlock + rb;
+      // -- loads: K (4 position tiles) and V (2 chunks x 8 rows) ----------
+      u32x4 kf[4][4];
+      u32x4 vrow[2][8];
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            kf[pt][s] = ld16(kb + (rb + 16 * pt + l16) * kts + (32 * s + 8 * g) * 2);
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            vrow[ch][j] = ld16(vb + (rb + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3)) * vts + 16 * l16);
+      } else {
+        u32x4 kr[4][2];
+        u32x2 vr[2][8];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          kr[pt][0] = ld16(kb + (rb + 16 * pt + l16) * kts + 32 * g);
+          kr[pt][1] = ld16(kb + (rb + 16 * pt + l16) * kts + 32 * g + 16);
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            vr[ch][j] = ld8(vb + (rb + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3)) * vts + 8 * l16);
+        if (pos0 + 63 > p_max) {
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (pos0 + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3) > p_max) vr[ch][j] = u32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const u32x4 w = kr[pt][s >> 1];
+            kf[pt][s] = fp8x8_to_bf16x8((s & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y});
+          }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vrow[ch][j] = fp8x8_to_bf16x8(vr[ch][j]);
+      }
+      // -- S^T = K Q^T -----------------------------------------------------
+      f32x4 sacc[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        sacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[pt] = mfma_bf16(kf[pt][s], qf[s], sacc[pt]);
+      }
+      // -- scale, causal/selection mask, online softmax ---------------------
+      float hmax = neg_inf();
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = pos0 + 16 * pt + 4 * g + i;
+          const float v = pos <= plim ? sacc[pt][i] * p.scale_log2 : neg_inf();
+          sacc[pt][i] = v;
+          hmax = fmaxf(hmax, v);
+        }
+      hmax = colgroup_max(hmax);
+      const float m_new = fmaxf(m_run, hmax);
+      const float m_use = m_new == neg_inf() ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      float lsum = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e2 = exp2f(sacc[pt][i] - m_use);
+          sacc[pt][i] = e2;
+          lsum += e2;
+        }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) O[T] *= alpha;
+      // -- V rows past every token of the wave hold no data: zero them ------
+      if constexpr (!FP8) {
+        if (pos0 + 63 > p_max) {
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (pos0 + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3) > p_max)
+                vrow[ch][j] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      // -- O^T += V^T P^T ---------------------------------------------------
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const f32x4 s0 = sacc[2 * ch], s1 = sacc[2 * ch + 1];
+        const u32x4 bp = {pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]),
+                          pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3])};
+#pragma unroll
+        for (int T = 0; T < 8; ++T) {
+          u32x4 a;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            a[q] = pick_halves(vrow[ch][2 * q][T >> 1], vrow[ch][2 * q + 1][T >> 1], T & 1);
+          O[T] = mfma_bf16(a, bp, O[T]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: normalise and store --------------------------------------
+  const float l_tot = colgroup_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!col_ok) return;
+  if (p.np == 1) {
+    uint16_t* op = p.out + ((size_t)qrow * p.H_q + hq) * kDim + 32 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = {pack_bf16(O[0][i] * inv, O[1][i] * inv), pack_bf16(O[2][i] * inv, O[3][i] * inv),
+                       pack_bf16(O[4][i] * inv, O[5][i] * inv), pack_bf16(O[6][i] * inv, O[7][i] * inv)};
+      *reinterpret_cast<u32x4*>(op + 8 * i) = v;
+    }
+  } else {
+    const size_t row = ((size_t)pi * p.rcap + qrow) * p.H_q + hq;
+    float* op = p.part_o + row * kDim + 32 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f32x4*>(op + 8 * i) = f32x4{O[0][i] * inv, O[1][i] * inv, O[2][i] * inv, O[3][i] * inv};
+      *reinterpret_cast<f32x4*>(op + 8 * i + 4) = f32x4{O[4][i] * inv, O[5][i] * inv, O[6][i] * inv, O[7][i] * inv};
+    }
+    if (g == 0) p.part_lse[row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+  }
+}
+
+size_t attention_decode_lds_bytes(const AttnParams& p) {
+  const int nbw = (p.nbmax + 31) / 32;
+  return (size_t)p.ntg * (p.tpw * nbw + 2 * p.tpw * p.top_k) * sizeof(uint32_t);
+}
+
+hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s) {
+  const int ntok_groups = (p.rg.max_seq + p.tpw - 1) / p.tpw;
+  const int ntgb = (ntok_groups + p.ntg - 1) / p.ntg;
+  const size_t nwg = (size_t)p.rg.batch * p.H_kv * ntgb * p.np;
+  const size_t lds = attention_decode_lds_bytes(p);
+  dim3 grid((unsigned)nwg), block(64 * p.ntg);
+  if (fp8) hipLaunchKernelGGL(attn_decode_kernel<true>, grid, block, lds, s, p);
+  else hipLaunchKernelGGL(attn_decode_kernel<false>, grid, block, lds, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K combine: out = sum_pi exp(lse_pi - LSE) o_pi / sum_pi exp(lse_pi -
+// LSE), partitions with lse = -inf skipped.  One workgroup per row slot,
+// 32 lanes per query head (4 dims each).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const int rs = blockIdx.x;
+  const int b = rs / p.max_seq, t = rs % p.max_seq;
+  const int r0 = p.offs[b];
+  if (t >= min(p.offs[b + 1] - r0, p.max_seq)) return;
+  const int r = r0 + t;
+  const int sub = threadIdx.x & 31;
+  for (int hq = threadIdx.x >> 5; hq < p.H_q; hq += 8) {
+    float M = neg_inf();
+    for (int pi = 0; pi < p.np; ++pi) M = fmaxf(M, p.part_lse[((size_t)pi * p.rcap + r) * p.H_q + hq]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (M != neg_inf()) {
+      for (int pi = 0; pi < p.np; ++pi) {
+        const size_t row = ((size_t)pi * p.rcap + r) * p.H_q + hq;
+        const float l = p.part_lse[row];
+        if (l == neg_inf()) continue;
+        const float w = __expf(l - M);
+        den += w;
+        const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + row * kDim + 4 * sub);
+        acc += w * o;
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const u32x2 v = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(p.out + ((size_t)r * p.H_q + hq) * kDim + 4 * sub) = v;
+  }
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+  dim3 grid((unsigned)((size_t)p.batch * p.max_seq));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace msa

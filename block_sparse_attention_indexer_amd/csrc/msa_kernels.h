@@ -1,0 +1,73 @@
+// Internal interface between the host API (msa_api.cpp) and the kernel
+// translation units.  Parameter blocks are passed to kernels by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// A paged cache as the kernels see it: base pointer and element strides.
+struct Pool {
+  const void* data;
+  int64_t page_stride, head_stride, token_stride;  // elements
+  int32_t num_pages;
+};
+
+// The ragged batch.
+struct Ragged {
+  const int32_t* offs;    // [B+1]
+  const int32_t* clen;    // [B]
+  const int32_t* table;   // [B][stride]
+  int32_t stride;
+  int32_t batch;
+  int32_t max_seq;
+};
+
+struct IndexerParams {
+  const uint16_t* q_idx;  // bf16 [R][H_kv][128]
+  Pool ik;                // bf16, H_ik heads
+  Ragged rg;
+  float* scores;          // [rcap][H_kv][nbmax]
+  int32_t* d_indices;     // [R][H_kv][top_k]
+  int32_t nbmax;
+  int32_t H_kv, H_ik;
+  int32_t top_k, init, local;
+};
+
+struct AttnParams {
+  const uint16_t* q;      // bf16 [R][H_q][128]
+  const int32_t* d_indices;
+  Pool k, v;
+  Ragged rg;
+  int32_t H_q, H_kv, G, top_k;
+  int32_t tpw;            // tokens per wave (decode / speculative route)
+  int32_t ntg;            // token groups (waves) per workgroup
+  int32_t np;             // split-K partitions
+  int32_t rcap;           // rows of the partial buffers (batch * max_seq)
+  int32_t nbmax;          // blocks a sequence may hold (bitmap size)
+  float scale_log2;       // softmax scale * log2(e)
+  uint16_t* out;          // bf16 [R][H_q][128]
+  float* part_o;          // [np][rcap][H_q][128]
+  float* part_lse;        // [np][rcap][H_q]
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* offs;
+  uint16_t* out;
+  int32_t batch, max_seq, np, H_q, rcap;
+};
+
+// Launchers; each returns hipSuccess or the launch error.
+hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
+hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s);
+hipError_t launch_topk(const IndexerParams& p, hipStream_t s);
+hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+// Bytes of LDS the decode attention kernel needs per workgroup.
+size_t attention_decode_lds_bytes(const AttnParams& p);
+
+}  // namespace msa

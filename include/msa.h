@@ -1,0 +1,250 @@
+/*
+ * msa.h -- C ABI of libmsa: block-sparse paged attention (MiniMax-M3 style
+ * "MSA") for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, as the "msa" module page of the MAX Mojo docs (graph-op
+ * bindings for the MiniMax-M3 MSA kernels) splits the method:
+ *
+ *   1. the indexer, which picks for every (new token, KV head) the KV blocks
+ *      that head may read, and
+ *   2. the sparse attention, which gathers only those blocks from a paged
+ *      KV cache and runs a causally clipped softmax over them,
+ *
+ * plus the split-K combine the attention uses when it splits a row's blocks
+ * over several partitions.
+ *
+ * Selection semantics follow the "ferrox_core::block_sparse" page (docs.rs),
+ * section "Four rules": a block's score is the maximum over its positions of
+ * the raw, unscaled dot product q_idx . k_idx; each KV head selects its own
+ * blocks and its whole GQA group reads them; the first `init_blocks` and the
+ * newest `local_blocks` blocks are always selected.  Section "The block size
+ * is an ABI, not a tuning knob" of the same page fixes blocks at 128 tokens,
+ * equal to the KV page size.
+ *
+ * Calling convention (all entry points):
+ *   - Output first, then inputs, then scalars, then the stream -- the
+ *     argument order of the ragged paged graph ops on the MAX pages.
+ *   - Every pointer named "device" is a device (HBM) address; every struct
+ *     is read on the host during the call and not kept.  The library never
+ *     allocates or frees memory and keeps no pointer after returning; the
+ *     caller owns every buffer and keeps it alive until the work queued on
+ *     `stream` has finished.
+ *   - `stream` is a hipStream_t passed as an opaque pointer (NULL: the null
+ *     stream).  All work is enqueued asynchronously on it; no call
+ *     synchronises with the device or copies device data to the host.
+ *   - Grid sizes depend only on host scalars (batch, max_seq_length,
+ *     max_cache_length, head counts, top_k, partitions), never on device
+ *     data, so a call can be captured into a HIP graph and replayed.
+ *   - Every argument is validated before anything is launched.  On a
+ *     validation error the call returns a negative MSA_ERR_* code and
+ *     enqueues nothing.  Device-data errors (a page id >= num_pages, a
+ *     cache length beyond the lookup table) are not detected: their result
+ *     is undefined.
+ *   - Calls are stateless and may be issued from several host threads.
+ *
+ * Data layout:
+ *   - Ragged rows: new token t of sequence b is global row
+ *     r = input_row_offsets[b] + t, at logical position
+ *     p = cache_lengths[b] + t (its K/V/index-K are already in the cache).
+ *     It may see the nb = p / 128 + 1 blocks 0 .. p/128 and positions
+ *     j <= p only ("msa" page, speculative-decode route: token position is
+ *     the cache length plus the token's index; causality is per token).
+ *   - Paged caches: logical position j of sequence b is slot j % 128 of page
+ *     kv_lookup_table[b * lookup_stride + j / 128].  Element d of head h of
+ *     that slot is at data + page*page_stride + h*head_stride
+ *     + slot*token_stride + d (strides in elements; d is contiguous).
+ *   - q_idx: bf16 [rows][num_kv_heads][128]; q and output: bf16
+ *     [rows][num_q_heads][128]; d_indices: int32 [rows][num_kv_heads][top_k];
+ *     all contiguous, 16-byte aligned.
+ *   - Query head g belongs to KV head g / (num_q_heads / num_kv_heads).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_NULL = -1,       /* a required pointer is NULL                          */
+    MSA_ERR_SHAPE = -2,      /* head_dim / page size != 128, head counts, strides,   */
+                             /* alignment, or a context beyond the supported maximum */
+    MSA_ERR_PARAM = -3,      /* top_k, init/local blocks, partitions, batch          */
+    MSA_ERR_DTYPE = -4,      /* unsupported storage type, or K and V types differ    */
+    MSA_ERR_WORKSPACE = -5,  /* workspace smaller than the *_workspace_bytes query    */
+    MSA_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch                    */
+    MSA_ERR_DEVICE = -7      /* no current HIP device, or it is not gfx950           */
+};
+
+/* Storage types of the paged caches ("msa" page: the index-K cache is always
+ * BF16; the main K/V cache is BF16 or native FP8 e4m3 with no scales). */
+enum msa_dtype {
+    MSA_DTYPE_BF16 = 0,
+    MSA_DTYPE_FP8_E4M3 = 1   /* OCP e4m3fn: bias 7, max 448, no inf, value x 1.0 */
+};
+
+enum {
+    MSA_BLOCK_SIZE = 128,    /* tokens per block == tokens per page */
+    MSA_HEAD_DIM = 128,      /* head dim of q, k, v, q_idx, k_idx   */
+    MSA_MAX_SPEC_DRAFT = 8,  /* max_seq_length 2..8 takes the speculative route */
+    MSA_MAX_BLOCKS = 8192,   /* most blocks one sequence may hold (1 Mi tokens) */
+    MSA_MAX_TOPK = 512
+};
+
+/* One paged cache (a page pool of one layer). */
+typedef struct msa_paged_cache {
+    const void* data;        /* device: page pool base, 16-byte aligned           */
+    int32_t dtype;           /* enum msa_dtype                                    */
+    int32_t num_pages;       /* pages in the pool                                 */
+    int32_t num_heads;       /* heads stored per page                             */
+    int32_t page_size;       /* must be 128 (MSA_BLOCK_SIZE)                      */
+    int32_t head_dim;        /* must be 128 (MSA_HEAD_DIM)                        */
+    int32_t reserved;        /* set to 0                                          */
+    int64_t page_stride;     /* elements between pages                            */
+    int64_t head_stride;     /* elements between heads of one page                */
+    int64_t token_stride;    /* elements between slots of one head                */
+} msa_paged_cache;
+
+/* The ragged batch: which rows are whose, and where their KV lives. */
+typedef struct msa_ragged {
+    const int32_t* input_row_offsets; /* device [batch+1]: prefix sums of new    */
+                                      /* tokens per sequence, [0] = 0            */
+    const int32_t* cache_lengths;     /* device [batch]: tokens cached before    */
+                                      /* this step's new tokens                  */
+    const int32_t* kv_lookup_table;   /* device [batch][lookup_stride]: page id  */
+                                      /* of each logical block                   */
+    int32_t lookup_stride;            /* entries per sequence in the table       */
+    int32_t batch;                    /* sequences                               */
+    int32_t max_seq_length;           /* host bound on new tokens per sequence;  */
+                                      /* picks the route: 1 decode, 2..8         */
+                                      /* speculative decode, > 8 prefill         */
+    int32_t max_cache_length;         /* host bound on cache_lengths[b]          */
+} msa_ragged;
+
+/* ------------------------------------------------------------------------ */
+/* Indexer                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes msa_indexer_paged needs for this batch shape.  Returns 0 on
+ * invalid arguments (and then msa_indexer_paged reports the error). */
+size_t msa_indexer_workspace_bytes(const msa_ragged* rg, int32_t num_kv_heads,
+                                   int32_t top_k);
+
+/*
+ * Block selection ("ferrox_core::block_sparse", "Four rules" section and the
+ * block_sparse_select function; "msa" page: the indexer emits top-k block
+ * ids per (index head, token)).
+ *
+ * For every row r (token at position p, nb visible blocks) and KV head h:
+ *   F = {0 .. min(init_blocks, nb)-1} U {max(0, nb-local_blocks) .. nb-1}.
+ *   If nb <= top_k the selection is every visible block 0 .. nb-1.
+ *   Otherwise every block outside F is scored with
+ *     s(blk) = max over j in blk, j <= p of  sum_d q_idx[r][h][d] * k_idx(j)[d]
+ *   (FP32 accumulation, no softmax scale), where k_idx(j) is head
+ *   h % index_k->num_heads of position j in the index-K cache, and the
+ *   top_k - |F| highest scores join F; equal scores go to the lower id.
+ *   d_indices[r][h][:] = the selection in ascending order, padded with -1.
+ *
+ * d_indices     device int32 [batch*max_seq_length rows max][num_kv_heads][top_k];
+ *               rows >= input_row_offsets[batch] are not written.
+ * q_idx         device bf16 [rows][num_kv_heads][128].
+ * index_k       BF16 cache with num_heads 1 (shared by all KV heads) or
+ *               num_kv_heads.
+ * top_k         1 .. MSA_MAX_TOPK; init_blocks, local_blocks >= 0 with
+ *               init_blocks + local_blocks <= top_k.
+ * workspace     device, >= msa_indexer_workspace_bytes(...) bytes.
+ *
+ * Errors: MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_PARAM, MSA_ERR_DTYPE,
+ * MSA_ERR_WORKSPACE, MSA_ERR_LAUNCH.  batch == 0 is a no-op.
+ */
+int msa_indexer_paged(int32_t* d_indices, const void* q_idx,
+                      const msa_paged_cache* index_k, const msa_ragged* rg,
+                      int32_t num_kv_heads, int32_t top_k, int32_t init_blocks,
+                      int32_t local_blocks, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse attention                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Number of split-K partitions msa_attention_paged uses for this shape when
+ * called with num_partitions (0 = automatic choice that fills the GPU's
+ * compute units).  Prefill (max_seq_length > 8) always uses 1.  Returns a
+ * negative MSA_ERR_* code on invalid arguments. */
+int msa_attention_partitions(const msa_ragged* rg, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t top_k,
+                             int32_t num_partitions);
+
+/* Workspace bytes msa_attention_paged needs (partials for the split-K
+ * combine, and the prefill plan).  Returns 0 on invalid arguments. */
+size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t top_k,
+                                     int32_t num_partitions);
+
+/*
+ * Sparse attention over the selected blocks ("ferrox_core::block_sparse",
+ * positions_of_blocks and the masked attention pass it feeds; "msa" page,
+ * routes: decode, speculative decode with per-token causality, prefill).
+ *
+ * For row r at position p and query head g of KV head h = g / G:
+ *   P   = { j : j / 128 in d_indices[r][h][:], j <= p }   (ids < 0 ignored)
+ *   out[r][g] = sum_{j in P} softmax_j(scale * q[r][g] . k(j)) v(j)
+ * with FP32 accumulation, rounded to BF16 (round to nearest even).  A row
+ * with no position in P gets 0.  Each row's ids must be distinct; their
+ * order does not matter.
+ *
+ * output        device bf16 [rows][num_q_heads][128]; rows >=
+ *               input_row_offsets[batch] are not written.
+ * q             device bf16 [rows][num_q_heads][128].
+ * d_indices     device int32 [rows][num_kv_heads][top_k] (the indexer's output).
+ * k_cache, v_cache  caches with num_heads == num_kv_heads and the same dtype
+ *               (BF16 or FP8 e4m3).
+ * num_q_heads   a multiple of num_kv_heads with group size 1, 2, 4, 8 or 16.
+ * scale         softmax scale applied to q.k (e.g. 1/sqrt(128)).
+ * num_partitions 0 = automatic, else 1 .. 64 (decode / speculative routes).
+ * workspace     device, >= msa_attention_workspace_bytes(...) bytes.
+ *
+ * When more than one partition is used the call enqueues the combine itself.
+ * Errors: as msa_indexer_paged.  batch == 0 is a no-op.
+ */
+int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
+                        const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                        const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t top_k, float scale, int32_t num_partitions,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Split-K combine ("msa" page: partials keyed on the ragged global query
+ * row; the shared combine writes the ragged output directly).
+ *
+ * Partition pi of row r, query head g holds its own normalised output
+ * o_pi = partial_o[pi][r][g][:] and the natural log of its softmax
+ * denominator lse_pi = partial_lse[pi][r][g] (-inf: no positions).  The
+ * result is sum_pi exp(lse_pi - LSE) o_pi with LSE = log sum_pi exp(lse_pi),
+ * rounded to BF16; 0 when every lse_pi is -inf.
+ *
+ * output        device bf16 [rows][num_q_heads][128].
+ * partial_o     device f32 [num_partitions][batch*max_seq_length][num_q_heads][128].
+ * partial_lse   device f32 [num_partitions][batch*max_seq_length][num_q_heads].
+ * input_row_offsets device int32 [batch+1].
+ *
+ * Errors: MSA_ERR_NULL, MSA_ERR_PARAM, MSA_ERR_LAUNCH.
+ */
+int msa_splitk_combine(void* output, const float* partial_o, const float* partial_lse,
+                       const int32_t* input_row_offsets, int32_t batch,
+                       int32_t max_seq_length, int32_t num_partitions,
+                       int32_t num_q_heads, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* msa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,99 @@
+"""The C ABI library: it loads, exports every declared entry point, and its
+host-side validation rejects bad arguments before touching any device.
+CPU only: none of these calls reaches a kernel launch or a device query."""
+import ctypes
+
+import pytest
+
+from block_sparse_attention_indexer_amd import binding as B
+
+OK, NULL, SHAPE, PARAM, DTYPE, WORKSPACE = 0, -1, -2, -3, -4, -5
+FAKE = 1 << 20        # a 16-byte aligned non-null address that is never dereferenced
+
+
+def test_library_exports_every_declared_function():
+    lib = B.library()
+    names = B.header_functions()
+    assert {"msa_indexer_paged", "msa_attention_paged", "msa_splitk_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def rg(batch=2, max_seq=1, max_cache=4000, stride=40, null=False):
+    p = None if null else FAKE
+    return B.Ragged(p, p, p, stride, batch, max_seq, max_cache)
+
+
+def cache(dtype=B.MSA_DTYPE_BF16, heads=1, page=128, dim=128, tok=128, data=FAKE):
+    return B.PagedCache(data, dtype, 100, heads, page, dim, 0, heads * 128 * tok, 128 * tok, tok)
+
+
+def indexer(r, c, heads=8, top_k=16, init=1, local=2, ws=0, d=FAKE, q=FAKE):
+    return B.library().msa_indexer_paged(d, q, ctypes.byref(c), ctypes.byref(r), heads, top_k, init,
+                                         local, FAKE if ws else None, ws, None)
+
+
+def attention(r, k, v, hq=64, hkv=8, top_k=16, np_=0, ws=0, out=FAKE, scale=0.1):
+    return B.library().msa_attention_paged(out, FAKE, FAKE, ctypes.byref(k), ctypes.byref(v),
+                                           ctypes.byref(r), hq, hkv, top_k, scale, np_,
+                                           FAKE if ws else None, ws, None)
+
+
+def test_indexer_validation():
+    assert indexer(rg(), cache(), d=None) == NULL
+    assert indexer(rg(null=True), cache()) == NULL
+    assert indexer(rg(), cache(data=None)) == NULL
+    assert indexer(rg(), cache(page=64)) == SHAPE
+    assert indexer(rg(), cache(dim=64)) == SHAPE
+    assert indexer(rg(), cache(heads=3)) == SHAPE
+    assert indexer(rg(), cache(tok=100)) == SHAPE            # unaligned stride
+    assert indexer(rg(), cache(data=FAKE + 2)) == SHAPE      # unaligned base
+    assert indexer(rg(), cache(dtype=B.MSA_DTYPE_FP8_E4M3)) == DTYPE
+    assert indexer(rg(), cache(dtype=7)) == DTYPE
+    assert indexer(rg(), cache(), top_k=0) == PARAM
+    assert indexer(rg(), cache(), top_k=2, init=2, local=1) == PARAM
+    assert indexer(rg(), cache(), init=-1) == PARAM
+    assert indexer(rg(max_cache=8192 * 128), cache()) == SHAPE
+    assert indexer(rg(), cache()) == NULL                    # scores buffer missing
+    assert indexer(rg(batch=0), cache()) == OK               # empty batch: no-op
+    need = B.msa_indexer_workspace_bytes(rg(), 8, 16)
+    assert need >= 2 * 8 * 32 * 4
+    assert indexer(rg(), cache(), ws=need - 1) == WORKSPACE
+    assert B.msa_indexer_workspace_bytes(rg(max_cache=1000), 8, 16) == 0   # nb <= top_k
+
+
+def test_attention_validation():
+    k = cache(heads=8)
+    v = cache(heads=8)
+    assert attention(rg(), k, v, out=None) == NULL
+    assert attention(rg(), k, v, hq=60) == SHAPE
+    assert attention(rg(), k, v, hq=8 * 32) == SHAPE              # group 32 unsupported
+    assert attention(rg(), cache(heads=4), v) == SHAPE
+    assert attention(rg(), cache(heads=8, dtype=B.MSA_DTYPE_FP8_E4M3), v) == DTYPE
+    assert attention(rg(), k, v, top_k=0) == PARAM
+    assert attention(rg(), k, v, np_=65) == PARAM
+    assert attention(rg(), k, v, scale=float("nan")) == PARAM
+    assert attention(rg(), k, v, np_=4) == NULL                 # partials missing
+    need = B.msa_attention_workspace_bytes(rg(), 64, 8, 16, 4)
+    assert attention(rg(), k, v, np_=4, ws=need - 1) == WORKSPACE
+    assert attention(rg(batch=0), k, v) == OK
+
+
+def test_partition_planning_is_host_only():
+    r = rg(batch=64, max_seq=1, max_cache=32767)
+    assert B.msa_attention_partitions(r, 64, 8, 16, 3) == 3
+    assert B.msa_attention_partitions(r, 64, 8, 16, 1) == 1
+    pre = rg(batch=4, max_seq=16384, max_cache=16384)
+    assert B.msa_attention_partitions(pre, 64, 8, 64, 0) == 1     # prefill never splits
+    assert B.msa_attention_workspace_bytes(pre, 64, 8, 64, 0) >= 0
+    ws = B.msa_attention_workspace_bytes(r, 64, 8, 16, 4)
+    assert ws >= 4 * 64 * 64 * 129 * 4
+    with pytest.raises(B.MsaError):
+        B.msa_attention_partitions(r, 64, 8, 16, 99)
+
+
+def test_combine_validation():
+    lib = B.library()
+    assert lib.msa_splitk_combine(FAKE, FAKE, FAKE, FAKE, 2, 1, 0, 8, None) == PARAM
+    assert lib.msa_splitk_combine(None, FAKE, FAKE, FAKE, 2, 1, 2, 8, None) == NULL
+    assert lib.msa_splitk_combine(FAKE, FAKE, FAKE, FAKE, 0, 1, 2, 8, None) == OK

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case generates seeded inputs on the GPU, runs msa_indexer_paged and
+msa_attention_paged, and compares (sampled) rows with the oracle element by
+element: block ids bit-exact on decisive rows (valid and within the score
+cut elsewhere), attention within the BF16 / FP8 tolerances on the oracle's
+own ids, and end to end on rows whose every head is decisive.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity
+from block_sparse_attention_indexer_amd import binding as B
+from block_sparse_attention_indexer_amd import inputs as I
+from oracle import msa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_and_check(wl, seqs=None, per_seq=None, num_partitions=0):
+    say(f"[case] {wl.name} B={wl.batch} seqs={seqs} per_seq={per_seq} np={num_partitions}")
+    inp = I.make_inputs(wl, DEV)
+    d_gpu = B.run_indexer(inp)
+    out_gpu = B.run_attention(inp, d_gpu, num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    seqs = list(range(wl.batch)) if seqs is None else list(seqs)
+    pb, orig_rows = O.problem_for_sequences(inp, seqs)
+    sub = parity.sample_rows(pb, per_seq)
+    d_ref, sels = O.indexer(pb, sub)
+    grows = torch.as_tensor(orig_rows[sub], device=DEV, dtype=torch.long)
+    nd, nr = parity.check_selection(pb, sub, d_gpu[grows].cpu().numpy(), sels)
+    d_mix = d_gpu.clone()
+    d_mix[grows] = torch.from_numpy(d_ref).to(DEV)
+    out_mix = B.run_attention(inp, d_mix, num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    ref = O.attention(pb, d_ref, sub)
+    err = parity.check_attention(out_mix[grows], ref, wl.kv_dtype, wl.name)
+    dec = [i for i, s in enumerate(sels) if all(x.decisive for x in s)]
+    if dec:
+        parity.check_attention(out_gpu[grows[dec]], ref[dec], wl.kv_dtype, wl.name + " end-to-end")
+    say(f"  rows={len(sub)} decisive heads={nd} relaxed={nr} max|err|={err:.3e}")
+    return inp, d_gpu, out_gpu
+
+
+def wl_custom(name, new, cached, H_kv=2, G=8, top_k=6, init=1, local=2, kv="bf16", H_ik=1,
+              boost=0.0, seed=3):
+    return I.Workload(name, new_lens=tuple(new), cache_lens=tuple(cached), num_kv_heads=H_kv,
+                      group=G, top_k=top_k, init_blocks=init, local_blocks=local, kv_dtype=kv,
+                      kv_sigma=0.5 if kv != "bf16" else 1.0, num_ik_heads=H_ik, boost_frac=boost,
+                      seed=seed)
+
+
+# --- the five workloads ------------------------------------------------------
+
+def test_decode_small_full():
+    run_and_check(I.decode_small())
+
+
+def test_decode_batch64_full_sampled():
+    run_and_check(I.decode_batch64(), seqs=[0, 1, 17, 40, 63])
+
+
+def test_spec_decode_full_sampled():
+    run_and_check(I.spec_decode(), seqs=[0, 5, 19, 31])
+
+
+def test_prefill_ragged_small():
+    wl = I.prefill_ragged(new=(300, 1100, 40, 2100), cached=(0, 2048, 5000, 16384))
+    run_and_check(wl, per_seq=40)
+
+
+def test_prefill_ragged_full_sampled():
+    run_and_check(I.prefill_ragged(), per_seq=24)
+
+
+def test_decode_fp8_long_full_sampled():
+    run_and_check(I.decode_fp8_long(), seqs=[0, 9, 15])
+
+
+# --- shape variants and edge cases -----------------------------------------
+
+@pytest.mark.parametrize("G", [1, 2, 4, 16])
+def test_group_sizes_decode_and_spec(G):
+    run_and_check(wl_custom(f"g{G}_decode", [1, 1, 1], [3000, 129, 5000], G=G))
+    run_and_check(wl_custom(f"g{G}_spec", [3, 8, 1, 5], [3000, 127, 5000, 2500], G=G, top_k=5))
+
+
+def test_separate_index_heads_and_no_forced_blocks():
+    run_and_check(wl_custom("ik_per_head", [1, 4], [4000, 2600], H_kv=4, H_ik=4, init=0, local=0,
+                            top_k=3))
+    run_and_check(wl_custom("local_only", [2, 1], [1300, 2000], init=0, local=1, top_k=2))
+
+
+def test_fp8_spec_and_boosted_rows():
+    run_and_check(wl_custom("fp8_spec", [2, 7], [6000, 700], kv="fp8_e4m3", top_k=8, local=4))
+    run_and_check(wl_custom("boost", [1, 1, 1, 1], [4095, 4096, 9000, 300], boost=0.05))
+
+
+def test_empty_and_zero_length_sequences():
+    wl = wl_custom("zero_len", [1, 0, 3, 0], [900, 700, 2000, 10], top_k=4)
+    run_and_check(wl)
+    inp = I.make_inputs(wl, DEV)
+    rg = B.ragged(inp.input_row_offsets[:1], inp.cache_lengths[:0], inp.kv_lookup_table[:0], 0, 0)
+    d = torch.empty((0, 2, 4), dtype=torch.int32, device=DEV)
+    B.msa_indexer_paged(d, inp.q_idx, inp.index_k, rg, 2, 4, 1, 2)
+
+
+@pytest.mark.parametrize("np_", [1, 2, 3, 7])
+def test_explicit_partitions(np_):
+    run_and_check(wl_custom(f"np{np_}", [1, 2, 5], [8000, 3000, 255], top_k=9), num_partitions=np_)
+
+
+def test_tie_break_lower_id_on_all_equal_scores():
+    wl = wl_custom("ties", [1, 2], [20 * 128 + 3, 9 * 128], top_k=6, init=1, local=2)
+    inp = I.make_inputs(wl, DEV)
+    inp.index_k.copy_(torch.ones_like(inp.index_k))
+    d = B.run_indexer(inp).cpu().numpy()
+    # row 0: nb 21 -> forced {0, 19, 20}, free {1, 2, 3}; rows 1, 2: nb 10, 10
+    assert list(d[0, 0]) == [0, 1, 2, 3, 19, 20]
+    assert list(d[1, 1]) == [0, 1, 2, 3, 8, 9]
+    assert list(d[2, 0]) == [0, 1, 2, 3, 8, 9]
+
+
+def test_page_permutation_gives_bitwise_identical_results():
+    wl = wl_custom("perm", [1, 3], [7000, 2000], top_k=8)
+    inp = I.make_inputs(wl, DEV)
+    d0 = B.run_indexer(inp)
+    o0 = B.run_attention(inp, d0)
+    P = inp.k_cache.shape[0]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(1)).to(DEV)
+    inv = torch.argsort(perm)
+    for name in ("index_k", "k_cache", "v_cache"):
+        setattr(inp, name, getattr(inp, name)[perm].contiguous())
+    inp.kv_lookup_table = inv[inp.kv_lookup_table.long()].to(torch.int32).contiguous()
+    d1 = B.run_indexer(inp)
+    o1 = B.run_attention(inp, d1)
+    torch.cuda.synchronize()
+    assert torch.equal(d0, d1)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
+def test_rows_fully_written_and_no_ids_gives_zero():
+    wl = wl_custom("poison", [1, 4], [3000, 500], top_k=5)
+    inp = I.make_inputs(wl, DEV)
+    d = B.run_indexer(inp)
+    out = torch.full((wl.total_rows + 3, wl.num_q_heads, 128), float("nan"), dtype=torch.bfloat16,
+                     device=DEV)
+    B.run_attention(inp, d, output=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:wl.total_rows].float()).all()
+    assert torch.isnan(out[wl.total_rows:].float()).all()
+    none = torch.full_like(d, -1)
+    B.run_attention(inp, none, output=out)
+    torch.cuda.synchronize()
+    assert (out[:wl.total_rows].float() == 0).all()
+
+
+def test_splitk_combine_standalone():
+    rng = np.random.default_rng(4)
+    np_, Bt, S, H = 5, 3, 4, 6
+    offs = np.array([0, 2, 2, 6], dtype=np.int32)
+    rcap = Bt * S
+    po = rng.standard_normal((np_, rcap, H, 128)).astype(np.float32)
+    pl = (rng.standard_normal((np_, rcap, H)) * 3).astype(np.float32)
+    pl[1] = -np.inf
+    pl[:, 0, 0] = -np.inf                     # a row/head with no positions at all
+    out = torch.full((6, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.msa_splitk_combine(out, torch.from_numpy(po).to(DEV), torch.from_numpy(pl).to(DEV),
+                         torch.from_numpy(offs).to(DEV), Bt, S, np_, H)
+    torch.cuda.synchronize()
+    # global rows are keyed on the ragged row: rows 0..5 live at 0..5
+    ref = O.splitk_combine(po[:, :6], pl[:, :6])
+    parity.check_attention(out, ref, "bf16", "combine")
+    assert (out[0, 0].float() == 0).all()
