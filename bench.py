@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse paged attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic inputs already resident
+in HBM: msa_indexer_paged (block-max scoring + top-k) then
+msa_attention_paged (sparse attention, plus the split-K combine when the row
+is split).  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_batch64]
+
+Default workload: decode, batch 64, 8 KV heads x GQA 8, context lengths
+uniform in [4096, 32768], top-k 16 (init 1, local 2), BF16 KV.  Its metric is
+the gathered-KV bytes the step must move divided by the step time (GB/s),
+with query tokens per second beside it; the prefill workload reports
+attention TFLOP/s instead.
+
+Roofline: the dominant kernel is the sparse-attention kernel.  Its average
+duration is measured live with HIP events on the launch stream over the
+timed region (the attention call minus a separately timed combine of the
+same shape, since the call enqueues both); achieved = algorithmic bytes (or
+flops) of one launch / that duration.
+
+CPU baseline: the oracle (plain NumPy, as written -- not tuned) timed on the
+host cores on a bounded sample of the same workload's rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_batch64",
+                    help="decode_small | decode_batch64 | spec_decode | prefill_ragged | "
+                         "decode_fp8_long | all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle work to sample for the CPU baseline")
+    ap.add_argument("--partitions", type=int, default=0, help="split-K partitions (0 = auto)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work, counted from the selections the step actually made
+# ---------------------------------------------------------------------------
+
+def algorithmic_work(wl, d_idx, rows=None):
+    """Gathered-KV bytes (union over a sequence's new tokens per KV head),
+    index-K bytes (non-forced candidate positions, once per sequence and
+    index-K head), attention flops (4 * D per (query head, position)) and
+    indexer flops (2 * D per (index head, candidate position)).  d_idx[i]
+    belongs to rows[i] (all rows in order when rows is None)."""
+    esz = 1 if wl.kv_dtype != "bf16" else 2
+    offs = np.concatenate([[0], np.cumsum(wl.new_lens)])
+    rows = np.arange(wl.total_rows) if rows is None else np.asarray(rows)
+    kv_bytes = ik_bytes = attn_flops = idx_flops = 0
+    for b in range(wl.batch):
+        sel = np.nonzero((rows >= offs[b]) & (rows < offs[b + 1]))[0]
+        if sel.size == 0:
+            continue
+        p = wl.cache_lens[b] + (rows[sel] - offs[b])
+        nb = p // 128 + 1
+        ids = d_idx[sel]                                  # [n, H_kv, top_k]
+        vis = np.where(ids >= 0, np.clip(p[:, None, None] - 128 * ids + 1, 0, 128), 0)
+        attn_flops += 4 * 128 * wl.group * int(vis.sum())
+        nbl = int(nb.max())
+        for h in range(wl.num_kv_heads):
+            cov = np.zeros(nbl + 1, dtype=np.int64)
+            m = ids[:, h] >= 0
+            np.maximum.at(cov, np.clip(ids[:, h][m], 0, nbl), vis[:, h][m])
+            kv_bytes += int(cov.sum()) * 128 * 2 * esz
+        if nbl > wl.top_k:
+            ik_bytes += max(0, nbl - wl.local_blocks - wl.init_blocks) * 128 * 256 * wl.num_ik_heads
+            k = np.where(nb > wl.top_k, nb - wl.local_blocks - wl.init_blocks, 0)
+            idx_flops += 2 * 128 * wl.num_kv_heads * 128 * int(k.sum())
+    return dict(kv_bytes=kv_bytes, ik_bytes=ik_bytes, attn_flops=attn_flops, idx_flops=idx_flops)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of rows
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(inp, wl, prefill, seconds):
+    from oracle import msa_oracle as O
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:  # pragma: no cover - reporting only
+        threads = 1
+    order = np.random.default_rng(0).permutation(wl.batch)
+    spent = 0.0
+    done_rows = 0
+    kv = flops = 0
+    seqs_used = []
+    for b in order:
+        pb, orig = O.problem_for_sequences(inp, [int(b)])
+        rows = list(range(len(orig)))
+        if prefill and len(rows) > 16:
+            rows = sorted(np.random.default_rng(int(b)).choice(len(orig), 16, replace=False).tolist())
+        t0 = time.perf_counter()
+        d, _ = O.indexer(pb, rows)
+        O.attention(pb, d, rows)
+        spent += time.perf_counter() - t0
+        full = np.full((wl.total_rows, wl.num_kv_heads, wl.top_k), -1, np.int32)
+        grows = [int(orig[r]) for r in rows]
+        full[grows] = d
+        w = algorithmic_work(wl, full[grows], rows=grows)
+        kv += w["kv_bytes"]
+        flops += w["attn_flops"]
+        done_rows += len(rows)
+        seqs_used.append(int(b))
+        if spent >= seconds:
+            break
+    if prefill:
+        value, unit = flops / spent / 1e12, "TFLOP/s"
+    else:
+        value, unit = kv / spent / 1e9, "GB/s"
+    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_rows} rows of {len(seqs_used)} of {wl.batch} sequences "
+                      f"({'16 sampled rows per sequence, ' if prefill else ''}"
+                      f"{spent:.1f} s of oracle time), selection + attention",
+            "query_tok_s": done_rows / spent,
+            "affinity_cpus": len(os.sched_getaffinity(0)), "os_cpus": os.cpu_count()}
+
+
+# ---------------------------------------------------------------------------
+# the measured step
+# ---------------------------------------------------------------------------
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("msa_attention.hip", "msa_common.h"):
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload):
+    """HBM traffic per launch of the attention kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"attn_decode_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run(workload, args):
+    import torch
+
+    from block_sparse_attention_indexer_amd import binding as B
+    from block_sparse_attention_indexer_amd import inputs as I
+
+    wl = I.WORKLOADS[workload]()
+    prefill = wl.max_seq_length > 8
+    inp = I.make_inputs(wl, "cuda")
+    rg = B.ragged_of_inputs(inp)
+    stream = torch.cuda.current_stream()
+    d = torch.empty((wl.total_rows, wl.num_kv_heads, wl.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.total_rows, wl.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    np_ = B.msa_attention_partitions(rg, wl.num_q_heads, wl.num_kv_heads, wl.top_k, args.partitions)
+    ws_i = torch.empty(max(1, B.msa_indexer_workspace_bytes(rg, wl.num_kv_heads, wl.top_k)),
+                       dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, B.msa_attention_workspace_bytes(rg, wl.num_q_heads, wl.num_kv_heads,
+                                                              wl.top_k, np_)),
+                       dtype=torch.uint8, device="cuda")
+
+    def indexer():
+        B.msa_indexer_paged(d, inp.q_idx, inp.index_k, rg, wl.num_kv_heads, wl.top_k,
+                            wl.init_blocks, wl.local_blocks, ws_i, stream)
+
+    def attention():
+        B.msa_attention_paged(out, inp.q, d, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
+                              wl.num_kv_heads, wl.top_k, wl.softmax_scale, np_, ws_a, stream)
+
+    for _ in range(args.warmup):
+        indexer()
+        attention()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        indexer()
+        ev[k][1].record(stream)
+        attention()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    # The attention call also enqueues the combine when np > 1: time a combine
+    # of the same shape on its own and subtract it.
+    comb_ms = 0.0
+    if np_ > 1:
+        rcap = wl.batch * wl.max_seq_length
+        po = torch.zeros((np_, rcap, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
+        pl = torch.zeros((np_, rcap, wl.num_q_heads), dtype=torch.float32, device="cuda")
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for k in range(K):
+            ce[k][0].record(stream)
+            B.msa_splitk_combine(out, po, pl, inp.input_row_offsets, wl.batch, wl.max_seq_length,
+                                 np_, wl.num_q_heads, stream)
+            ce[k][1].record(stream)
+        torch.cuda.synchronize()
+        comb_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ce]))
+        attention()                       # restore the real output
+        torch.cuda.synchronize()
+    attn_kernel_ms = max(att_ms - comb_ms, 1e-6)
+
+    work = algorithmic_work(wl, d.cpu().numpy())
+    ms = wall / K * 1e3
+    tok_s = wl.total_rows / (wall / K)
+    if prefill:
+        metric_value = work["attn_flops"] / (wall / K) / 1e12
+        unit = "TFLOP/s"
+        achieved = work["attn_flops"] / (attn_kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+    else:
+        metric_value = work["kv_bytes"] / (wall / K) / 1e9
+        unit = "GB/s"
+        achieved = work["kv_bytes"] / (attn_kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload)}
+    res = {
+        "metric": "decode gathered-KV GB/s (% HBM peak) + query tok/s; prefill TFLOP/s (% MFMA)",
+        "value": metric_value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.kv_dtype == "bf16" else "fp8_e4m3 kv / bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.total_rows,
+                   "max_context": max(wl.seq_lens()), "kv_heads": wl.num_kv_heads,
+                   "gqa": wl.group, "top_k": wl.top_k, "init_blocks": wl.init_blocks,
+                   "local_blocks": wl.local_blocks, "kv_dtype": wl.kv_dtype,
+                   "index_k_heads": wl.num_ik_heads, "split_k_partitions": np_},
+        "query_tok_s": tok_s,
+        "hbm_frac_of_step": (work["kv_bytes"] + work["ik_bytes"]) / (wall / K) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_ms": {"indexer_call": idx_ms, "attention_call": att_ms, "combine": comb_ms,
+                       "attention_kernel": attn_kernel_ms},
+        "algorithmic": work,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, wl, prefill, args.cpu_seconds)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path; "
+                         "run with --gpus 1\n")
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long"]
+             if args.workload == "all" else [args.workload])
+    for name in names:
+        print(json.dumps(run(name, args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

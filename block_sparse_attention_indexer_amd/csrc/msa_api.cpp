@@ -194,11 +194,11 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   if (st != MSA_OK) return st;
   if ((st = check_selection(top_k, init_blocks, local_blocks)) != MSA_OK) return st;
   if (num_kv_heads < 1) return MSA_ERR_SHAPE;
+  if (empty_batch(*rg)) return MSA_OK;   // no rows: buffers may be empty (null)
   if ((st = check_cache(index_k, false)) != MSA_OK) return st;
   if (index_k->num_heads != 1 && index_k->num_heads != num_kv_heads) return MSA_ERR_SHAPE;
   if (!d_indices || !q_idx) return MSA_ERR_NULL;
   if (!aligned16(q_idx) || !aligned16(d_indices)) return MSA_ERR_SHAPE;
-  if (empty_batch(*rg)) return MSA_OK;
   const size_t need = indexer_ws(*rg, num_kv_heads, top_k);
   if (need && !workspace) return MSA_ERR_NULL;
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
@@ -255,6 +255,7 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   if (top_k < 1 || top_k > MSA_MAX_TOPK) return MSA_ERR_PARAM;
   if (num_partitions < 0 || num_partitions > kMaxPartitions) return MSA_ERR_PARAM;
   if (!(scale == scale)) return MSA_ERR_PARAM;
+  if (empty_batch(*rg)) return MSA_OK;   // no rows: buffers may be empty (null)
   if ((st = check_cache(k_cache, true)) != MSA_OK) return st;
   if ((st = check_cache(v_cache, true)) != MSA_OK) return st;
   if (k_cache->dtype != v_cache->dtype) return MSA_ERR_DTYPE;
@@ -262,7 +263,6 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_SHAPE;
   if (!output || !q || !d_indices) return MSA_ERR_NULL;
   if (!aligned16(output) || !aligned16(q) || !aligned16(d_indices)) return MSA_ERR_SHAPE;
-  if (empty_batch(*rg)) return MSA_OK;
   // The automatic partition count depends on the device's CU count; an
   // explicit one does not, so its workspace is checked before any device query.
   int cus = 0;

@@ -294,40 +294,56 @@ hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Split-K combine: out = sum_pi exp(lse_pi - LSE) o_pi / sum_pi exp(lse_pi -
-// LSE), partitions with lse = -inf skipped.  One workgroup per row slot,
-// 32 lanes per query head (4 dims each).
+// LSE), partitions with lse = -inf skipped.  One workgroup per (row slot,
+// 8 query heads); 32 lanes per head, 4 dims per lane.  Lane i of a head's
+// group reads lse of partitions i and i + 32, so the weights come from one
+// load and a 32-lane reduction; the partial outputs are then read with all
+// loads of a pass in flight.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  const int rs = blockIdx.x;
+  const int hgroups = (p.H_q + 7) >> 3;
+  const int rs = blockIdx.x / hgroups;
+  const int hq = (blockIdx.x % hgroups) * 8 + (threadIdx.x >> 5);
   const int b = rs / p.max_seq, t = rs % p.max_seq;
   const int r0 = p.offs[b];
-  if (t >= min(p.offs[b + 1] - r0, p.max_seq)) return;
+  if (t >= min(p.offs[b + 1] - r0, p.max_seq) || hq >= p.H_q) return;
   const int r = r0 + t;
   const int sub = threadIdx.x & 31;
-  for (int hq = threadIdx.x >> 5; hq < p.H_q; hq += 8) {
-    float M = neg_inf();
-    for (int pi = 0; pi < p.np; ++pi) M = fmaxf(M, p.part_lse[((size_t)pi * p.rcap + r) * p.H_q + hq]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (M != neg_inf()) {
-      for (int pi = 0; pi < p.np; ++pi) {
-        const size_t row = ((size_t)pi * p.rcap + r) * p.H_q + hq;
-        const float l = p.part_lse[row];
-        if (l == neg_inf()) continue;
-        const float w = __expf(l - M);
-        den += w;
-        const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + row * kDim + 4 * sub);
-        acc += w * o;
-      }
+  const size_t stride = (size_t)p.rcap * p.H_q;          // between partitions
+  const size_t base = (size_t)r * p.H_q + hq;
+  const float l0 = sub < p.np ? p.part_lse[sub * stride + base] : neg_inf();
+  const float l1 = sub + 32 < p.np ? p.part_lse[(sub + 32) * stride + base] : neg_inf();
+  float M = fmaxf(l0, l1);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+  const float w0 = l0 == neg_inf() ? 0.f : __expf(l0 - M);
+  const float w1 = l1 == neg_inf() ? 0.f : __expf(l1 - M);
+  float den = w0 + w1;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) den += __shfl_xor(den, o, 32);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = p.part_o + base * kDim + 4 * sub;
+  for (int pi0 = 0; pi0 < p.np; pi0 += 8) {
+    f32x4 v[8];
+    float w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int pi = pi0 + k;
+      w[k] = pi < 32 ? __shfl(w0, pi, 32) : __shfl(w1, pi - 32, 32);
+      v[k] = (pi < p.np && w[k] != 0.f) ? *reinterpret_cast<const f32x4*>(po + pi * stride * kDim)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    const u32x2 v = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
-    *reinterpret_cast<u32x2*>(p.out + ((size_t)r * p.H_q + hq) * kDim + 4 * sub) = v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (pi0 + k < p.np) acc += w[k] * v[k];
   }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const u32x2 o = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(p.out + base * kDim + 4 * sub) = o;
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  dim3 grid((unsigned)((size_t)p.batch * p.max_seq));
+  dim3 grid((unsigned)((size_t)p.batch * p.max_seq * ((p.H_q + 7) / 8)));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
