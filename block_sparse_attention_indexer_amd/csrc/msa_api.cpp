@@ -110,11 +110,24 @@ bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 
 // ---- indexer ---------------------------------------------------------------
 
+// Prefill indexer tiles: the index-K head count is only known with the
+// cache; the work list is sized for the worst case (one head per KV head).
+size_t indexer_items(const msa_ragged& rg, int32_t num_kv_heads, int32_t H_ik) {
+  const int tq = prefill_indexer_tile(num_kv_heads, H_ik);
+  return (size_t)rg.batch * ((rg.max_seq_length + tq - 1) / tq) * H_ik;
+}
+
 size_t indexer_ws(const msa_ragged& rg, int32_t num_kv_heads, int32_t top_k) {
   if (empty_batch(rg)) return 0;
   const int64_t nb = max_blocks(rg);
   if (nb <= top_k) return 0;     // every row selects all of its blocks
-  return align_up((size_t)row_capacity(rg) * num_kv_heads * nb * sizeof(float));
+  const size_t stride = (size_t)(nb + 15) / 16 * 16;
+  size_t ws = align_up((size_t)row_capacity(rg) * num_kv_heads * stride * sizeof(float));
+  if (route_of(rg) == Route::Prefill)
+    ws += align_up(2 * sizeof(int32_t)) +
+          align_up(std::max(indexer_items(rg, num_kv_heads, 1), indexer_items(rg, num_kv_heads, num_kv_heads)) *
+                   sizeof(int32_t));
+  return ws;
 }
 
 // ---- attention ---------------------------------------------------------------
@@ -150,8 +163,29 @@ AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int re
   return pl;
 }
 
-size_t attention_ws(const msa_ragged& rg, int H_q, int np) {
-  if (empty_batch(rg) || np <= 1) return 0;
+// Prefill tiles: tokens per tile for group size G (the kernels' choice).
+int prefill_tokens_per_tile(int G) {
+  AttnParams p{};
+  p.G = G;
+  int tq = 0, nct = 0;
+  prefill_tiling(p, &tq, &nct);
+  return tq;
+}
+
+size_t prefill_plan_slots(const msa_ragged& rg, int G, int H_kv) {
+  const int tq = prefill_tokens_per_tile(G);
+  return (size_t)rg.batch * ((rg.max_seq_length + tq - 1) / tq) * H_kv;
+}
+
+size_t attention_ws(const msa_ragged& rg, int H_q, int H_kv, int np) {
+  if (empty_batch(rg)) return 0;
+  if (route_of(rg) == Route::Prefill) {
+    const size_t slots = prefill_plan_slots(rg, H_q / H_kv, H_kv);
+    const size_t nb = (size_t)max_blocks(rg);
+    return 2 * align_up(slots * sizeof(int32_t)) + align_up(2 * sizeof(int32_t)) +
+           3 * align_up(slots * nb * sizeof(int32_t));
+  }
+  if (np <= 1) return 0;
   const size_t rows = (size_t)np * row_capacity(rg) * H_q;
   return align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
 }
@@ -211,6 +245,7 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   p.scores = static_cast<float*>(workspace);
   p.d_indices = d_indices;
   p.nbmax = (int32_t)max_blocks(*rg);
+  p.score_stride = (p.nbmax + 15) / 16 * 16;
   p.H_kv = num_kv_heads;
   p.H_ik = index_k->num_heads;
   p.top_k = top_k;
@@ -218,7 +253,22 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   p.local = local_blocks;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.nbmax > top_k) {
-    if (launch_indexer_decode(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
+    hipError_t e;
+    if (route_of(*rg) == Route::Prefill) {
+      int cus = 0;
+      if ((st = current_device(&cus)) != MSA_OK) return st;
+      p.tq = prefill_indexer_tile(num_kv_heads, p.H_ik);
+      p.ntiles = (rg->max_seq_length + p.tq - 1) / p.tq;
+      const size_t stride = (size_t)p.score_stride;
+      char* w = static_cast<char*>(workspace) +
+                align_up((size_t)row_capacity(*rg) * num_kv_heads * stride * sizeof(float));
+      p.sched = reinterpret_cast<int32_t*>(w);
+      p.worklist = reinterpret_cast<int32_t*>(w + align_up(2 * sizeof(int32_t)));
+      e = launch_indexer_prefill(p, cus, s);
+    } else {
+      e = launch_indexer_decode(p, s);
+    }
+    if (e != hipSuccess) return MSA_ERR_LAUNCH;
   }
   if (launch_topk(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
   return MSA_OK;
@@ -241,7 +291,7 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t top_k, int32_t num_partitions) {
   const int np = msa_attention_partitions(rg, num_q_heads, num_kv_heads, top_k, num_partitions);
   if (np < 1) return 0;
-  return attention_ws(*rg, num_q_heads, np);
+  return attention_ws(*rg, num_q_heads, num_kv_heads, np);
 }
 
 int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
@@ -254,7 +304,7 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   if ((st = check_heads(num_q_heads, num_kv_heads)) != MSA_OK) return st;
   if (top_k < 1 || top_k > MSA_MAX_TOPK) return MSA_ERR_PARAM;
   if (num_partitions < 0 || num_partitions > kMaxPartitions) return MSA_ERR_PARAM;
-  if (!(scale == scale)) return MSA_ERR_PARAM;
+  if (!(scale > 0.f) || scale > 3.0e38f) return MSA_ERR_PARAM;   // positive and finite
   if (empty_batch(*rg)) return MSA_OK;   // no rows: buffers may be empty (null)
   if ((st = check_cache(k_cache, true)) != MSA_OK) return st;
   if ((st = check_cache(v_cache, true)) != MSA_OK) return st;
@@ -269,10 +319,10 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   if (num_partitions == 0 && (st = current_device(&cus)) != MSA_OK) return st;
   const int G = num_q_heads / num_kv_heads;
   const AttnPlan pl = plan_attention(*rg, G, num_kv_heads, top_k, num_partitions, cus);
-  const size_t need = attention_ws(*rg, num_q_heads, pl.np);
+  const size_t need = attention_ws(*rg, num_q_heads, num_kv_heads, pl.np);
   if (need && !workspace) return MSA_ERR_NULL;
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
-  if (num_partitions != 0 && (st = current_device(nullptr)) != MSA_OK) return st;
+  if (num_partitions != 0 && (st = current_device(&cus)) != MSA_OK) return st;
 
   AttnParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -291,6 +341,30 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   p.nbmax = (int32_t)max_blocks(*rg);
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.out = static_cast<uint16_t*>(output);
+  const bool fp8 = k_cache->dtype == MSA_DTYPE_FP8_E4M3;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (route_of(*rg) == Route::Prefill) {
+    int nct = 0;
+    prefill_tiling(p, &p.tq, &nct);
+    p.ntiles = (rg->max_seq_length + p.tq - 1) / p.tq;
+    const size_t slots = prefill_plan_slots(*rg, G, num_kv_heads);
+    char* w = static_cast<char*>(workspace);
+    p.plan_cnt = reinterpret_cast<int32_t*>(w);
+    w += align_up(slots * sizeof(int32_t));
+    p.plan_ids = reinterpret_cast<int32_t*>(w);
+    w += align_up(slots * (size_t)p.nbmax * sizeof(int32_t));
+    p.plan_pages = reinterpret_cast<int32_t*>(w);
+    w += align_up(slots * (size_t)p.nbmax * sizeof(int32_t));
+    p.plan_mask = reinterpret_cast<uint32_t*>(w);
+    w += align_up(slots * (size_t)p.nbmax * sizeof(int32_t));
+    p.worklist = reinterpret_cast<int32_t*>(w);
+    w += align_up(slots * sizeof(int32_t));
+    p.sched = reinterpret_cast<int32_t*>(w);
+    p.nwg = cus;   // one 142 KiB workgroup per CU
+    if ((size_t)(p.nbmax + 1) * sizeof(uint32_t) > kMaxLds) return MSA_ERR_SHAPE;
+    if (launch_attention_prefill(p, fp8, s) != hipSuccess) return MSA_ERR_LAUNCH;
+    return MSA_OK;
+  }
   if (pl.np > 1) {
     const size_t rows = (size_t)pl.np * p.rcap * num_q_heads;
     p.part_o = static_cast<float*>(workspace);
@@ -298,9 +372,7 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
                                           align_up(rows * MSA_HEAD_DIM * sizeof(float)));
   }
   if (attention_decode_lds_bytes(p) > kMaxLds) return MSA_ERR_PARAM;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_attention_decode(p, k_cache->dtype == MSA_DTYPE_FP8_E4M3, s) != hipSuccess)
-    return MSA_ERR_LAUNCH;
+  if (launch_attention_decode(p, fp8, s) != hipSuccess) return MSA_ERR_LAUNCH;
   if (pl.np > 1) {
     CombineParams c{p.part_o, p.part_lse, rg->input_row_offsets, p.out, rg->batch,
                     rg->max_seq_length, pl.np, num_q_heads, p.rcap};

@@ -94,4 +94,9 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// 2^x with the hardware instruction (v_exp_f32): exact at 0, 0 at -inf,
+// ~1 ulp elsewhere; results below the normal range flush to 0, which only
+// affects probabilities under 2^-126.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 }  // namespace msa

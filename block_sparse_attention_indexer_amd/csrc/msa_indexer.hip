@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const float m = colgroup_max(mx[ct]);
-      if (g == 0 && plim[ct] >= 0) p.scores[(size_t)orow[ct] * p.nbmax + blk] = m;
+      if (g == 0 && plim[ct] >= 0) p.scores[(size_t)orow[ct] * p.score_stride + blk] = m;
     }
   }
 }
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   for (int i = lane; i < p.local; i += 64) out[p.init + kfree + i] = nb - p.local + i;
   if (kfree == 0) return;
 
-  const float* sc = p.scores + ((size_t)r * p.H_kv + h) * p.nbmax + p.init;
+  const float* sc = p.scores + ((size_t)r * p.H_kv + h) * p.score_stride + p.init;
   const int nslot = (ncand + 63) / 64;
   uint32_t key[KPL];
 #pragma unroll

@@ -28,9 +28,14 @@ struct IndexerParams {
   const uint16_t* q_idx;  // bf16 [R][H_kv][128]
   Pool ik;                // bf16, H_ik heads
   Ragged rg;
-  float* scores;          // [rcap][H_kv][nbmax]
+  float* scores;          // [rcap][H_kv][score_stride]
   int32_t* d_indices;     // [R][H_kv][top_k]
   int32_t nbmax;
+  int32_t score_stride;   // nbmax rounded up to 16
+  // prefill route: tiles of tq tokens, scheduled through a device work list
+  int32_t tq, ntiles;     // tokens per tile, tiles per sequence
+  int32_t* worklist;      // [B * ntiles * H_ik] tile items, heaviest first
+  int32_t* sched;         // [0] items in the list, [1] next item to take
   int32_t H_kv, H_ik;
   int32_t top_k, init, local;
 };
@@ -50,6 +55,15 @@ struct AttnParams {
   uint16_t* out;          // bf16 [R][H_q][128]
   float* part_o;          // [np][rcap][H_q][128]
   float* part_lse;        // [np][rcap][H_q]
+  // prefill route: tiles of tq tokens and the device-built plan
+  int32_t tq, ntiles;     // tokens per tile, tiles per sequence
+  int32_t* plan_cnt;      // [B][ntiles][H_kv] union size
+  int32_t* plan_ids;      // [B][ntiles][H_kv][nbmax] ascending block ids
+  int32_t* plan_pages;    // [B][ntiles][H_kv][nbmax] page id of each block
+  uint32_t* plan_mask;    // [B][ntiles][H_kv][nbmax] token mask per block
+  int32_t* worklist;      // [B * ntiles * H_kv] non-empty plan slots, heaviest first
+  int32_t* sched;         // [0] slots in the list, [1] next slot to take
+  int32_t nwg;            // persistent workgroups launched
 };
 
 struct CombineParams {
@@ -62,10 +76,16 @@ struct CombineParams {
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
-hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s);
+hipError_t launch_indexer_prefill(const IndexerParams& p, int num_cus, hipStream_t s);
+int prefill_indexer_tile(int H_kv, int H_ik);
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s);
 hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s);
+
+// Tokens per tile (tq) and MFMA column tiles per wave of the prefill
+// attention for group size p.G.
+void prefill_tiling(const AttnParams& p, int* tq, int* nct);
 
 // Bytes of LDS the decode attention kernel needs per workgroup.
 size_t attention_decode_lds_bytes(const AttnParams& p);

@@ -205,7 +205,8 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
  * k_cache, v_cache  caches with num_heads == num_kv_heads and the same dtype
  *               (BF16 or FP8 e4m3).
  * num_q_heads   a multiple of num_kv_heads with group size 1, 2, 4, 8 or 16.
- * scale         softmax scale applied to q.k (e.g. 1/sqrt(128)).
+ * scale         softmax scale applied to q.k (e.g. 1/sqrt(128)); positive
+ *               and finite.
  * num_partitions 0 = automatic, else 1 .. 64 (decode / speculative routes).
  * workspace     device, >= msa_attention_workspace_bytes(...) bytes.
  *

@@ -73,6 +73,9 @@ def test_attention_validation():
     assert attention(rg(), k, v, top_k=0) == PARAM
     assert attention(rg(), k, v, np_=65) == PARAM
     assert attention(rg(), k, v, scale=float("nan")) == PARAM
+    assert attention(rg(), k, v, scale=0.0) == PARAM
+    assert attention(rg(), k, v, scale=-0.1) == PARAM
+    assert attention(rg(), k, v, scale=float("inf")) == PARAM
     assert attention(rg(), k, v, np_=4) == NULL                 # partials missing
     need = B.msa_attention_workspace_bytes(rg(), 64, 8, 16, 4)
     assert attention(rg(), k, v, np_=4, ws=need - 1) == WORKSPACE

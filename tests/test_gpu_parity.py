@@ -179,3 +179,29 @@ def test_splitk_combine_standalone():
     ref = O.splitk_combine(po[:, :6], pl[:, :6])
     parity.check_attention(out, ref, "bf16", "combine")
     assert (out[0, 0].float() == 0).all()
+
+
+# --- prefill route variants --------------------------------------------------
+
+@pytest.mark.parametrize("G", [1, 2, 4, 16])
+def test_prefill_group_sizes(G):
+    run_and_check(wl_custom(f"prefill_g{G}", [40, 100, 9], [0, 3000, 700], G=G, top_k=6),
+                  per_seq=30)
+
+
+def test_prefill_fp8_kv():
+    run_and_check(wl_custom("prefill_fp8", [70, 33], [2500, 0], kv="fp8_e4m3", top_k=7, local=3),
+                  per_seq=30)
+
+
+def test_prefill_index_head_per_kv_head_and_no_forced_blocks():
+    run_and_check(wl_custom("prefill_ik_per_head", [300, 20], [1000, 5000], H_kv=2, H_ik=2,
+                            top_k=5, init=0, local=0), per_seq=40)
+    run_and_check(wl_custom("prefill_local_only", [150], [3000], top_k=4, init=0, local=1),
+                  per_seq=40)
+
+
+def test_prefill_tile_edges():
+    # lengths around the 32-token tile and the 128-token block
+    run_and_check(wl_custom("prefill_edges", [9, 31, 32, 33, 129], [127, 128, 0, 4000, 255],
+                            top_k=4), per_seq=None)
