@@ -163,17 +163,17 @@ AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int re
   return pl;
 }
 
-// Prefill tiles: tokens per tile for group size G (the kernels' choice).
-int prefill_tokens_per_tile(int G) {
-  AttnParams p{};
-  p.G = G;
+// Prefill tiles: tokens per tile for group size G and KV type (the kernels'
+// choice).  Workspace is sized for the smaller tile of the two types, since
+// the size query does not know the type.
+int prefill_tokens_per_tile(int G, bool fp8) {
   int tq = 0, nct = 0;
-  prefill_tiling(p, &tq, &nct);
+  prefill_tiling(G, fp8, &tq, &nct);
   return tq;
 }
 
 size_t prefill_plan_slots(const msa_ragged& rg, int G, int H_kv) {
-  const int tq = prefill_tokens_per_tile(G);
+  const int tq = std::min(prefill_tokens_per_tile(G, false), prefill_tokens_per_tile(G, true));
   return (size_t)rg.batch * ((rg.max_seq_length + tq - 1) / tq) * H_kv;
 }
 
@@ -345,7 +345,7 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (route_of(*rg) == Route::Prefill) {
     int nct = 0;
-    prefill_tiling(p, &p.tq, &nct);
+    prefill_tiling(G, fp8, &p.tq, &nct);
     p.ntiles = (rg->max_seq_length + p.tq - 1) / p.tq;
     const size_t slots = prefill_plan_slots(*rg, G, num_kv_heads);
     char* w = static_cast<char*>(workspace);

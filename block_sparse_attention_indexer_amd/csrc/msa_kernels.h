@@ -84,8 +84,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s);
 
 // Tokens per tile (tq) and MFMA column tiles per wave of the prefill
-// attention for group size p.G.
-void prefill_tiling(const AttnParams& p, int* tq, int* nct);
+// attention for group size G and KV storage type.
+void prefill_tiling(int G, bool fp8, int* tq, int* nct);
 
 // Bytes of LDS the decode attention kernel needs per workgroup.
 size_t attention_decode_lds_bytes(const AttnParams& p);

@@ -21,6 +21,8 @@
 // issued before block e is computed and written to LDS after it, with the
 // raw bits held in registers in between (any conversion happens at the LDS
 // store so that the loads stay in flight during the compute).
+#include <algorithm>
+
 #include "msa_common.h"
 #include "msa_kernels.h"
 
@@ -673,10 +675,312 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnParams p) {
   }
 }
 
-void prefill_tiling(const AttnParams& p, int* tq, int* nct) {
-  *tq = p.G >= 16 ? 16 : 32;
-  const int cpw = *tq * p.G / kPrefillWaves;
-  *nct = cpw > 16 ? 2 : 1;
+// ---------------------------------------------------------------------------
+// BF16 prefill attention with direct global->LDS tile loads.
+//
+// Workgroup = 8 waves (two per SIMD) of 16 * NCT columns each.  K and V tiles are DMA'd
+// straight into LDS, row-major, 256-byte rows with 16-byte column c of row
+// pos stored at column c ^ (pos & 15); each lane of a DMA instruction picks
+// its source so that its fixed LDS slot receives the right swizzled piece.
+// The PV A-operand (V^T) comes from two ds_read_b64_tr_b16 per fragment:
+// within each 16-lane group, output lane i, element k is element i % 4 of
+// source lane i / 4 + 4k, so source lane j reads row 16r + 4g + j / 4 at
+// dims 16dt + 4(j % 4), which yields for lane (m, g) the positions
+// 16r + 4g + k of dim 16dt + m -- exactly the P^T B-operand layout.
+// ---------------------------------------------------------------------------
+constexpr int kP3Waves = 8;
+constexpr float kLazy = 8.f;   // log2 headroom before the running max moves
+
+struct PrefillLds3 {
+  char k[2][kBlock * 256];
+  char v[2][kBlock * 256];
+  int32_t ring_blk[2 * kRingHalf], ring_pg[2 * kRingHalf];
+  uint32_t ring_msk[2 * kRingHalf];
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ u32x2 lds_tr8(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_char*)lds_dst, 16, 0, 0);
+}
+
+template <int NCT>
+__device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int h = slot % p.H_kv;
+  const int tile = (slot / p.H_kv) % p.ntiles;
+  const int b = slot / p.H_kv / p.ntiles;
+  const int r0 = p.rg.offs[b];
+  const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
+  const int t0 = tile * p.tq;
+  if (t0 >= n) return;
+  const int c = p.rg.clen[b];
+  const int ntok = min(p.tq, n - t0);
+  const int p_tile_max = c + t0 + ntok - 1;
+  const int cnt = p.plan_cnt[slot];
+  const int32_t* ids = p.plan_ids + (size_t)slot * p.nbmax;
+  const int32_t* pgs = p.plan_pages + (size_t)slot * p.nbmax;
+  const uint32_t* msks = p.plan_mask + (size_t)slot * p.nbmax;
+
+  // ---- columns of this wave ---------------------------------------------
+  const int cpw = p.tq * p.G / kP3Waves;            // columns per wave (<= 16 * NCT)
+  const int tok_lo = wave * cpw / p.G;
+  const int tok_n = max(1, cpw / p.G);
+  uint32_t wave_bits = 0u;
+  for (int t = tok_lo; t < tok_lo + tok_n && t < ntok; ++t) wave_bits |= 1u << t;
+  int plim_col[NCT], tl_col[NCT];
+  u32x4 qf[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int cw = ct * 16 + l16;
+    const int cg = wave * cpw + cw;
+    tl_col[ct] = cg / p.G;
+    const bool ok = cw < cpw && tl_col[ct] < ntok;
+    plim_col[ct] = ok ? c + t0 + tl_col[ct] : -1;
+    const uint16_t* qp = p.q + ((size_t)(r0 + t0 + tl_col[ct]) * p.H_q + h * p.G + cg % p.G) * kDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[ct][s] = ok ? ld16(qp + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const int p_wave_min = c + t0 + tok_lo;
+
+  f32x4 O[8][NCT];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NCT], l_run[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    m_run[ct] = neg_inf();
+    l_run[ct] = 0.f;
+  }
+  const float sc = p.scale_log2;
+
+  // ---- lane-constant LDS addresses ---------------------------------------
+  // K A-operand: row 16pt + l16 (+ 64hb), logical column 4s + g
+  //   = l16 * 256 + ((4s + g) ^ l16) * 16 = kq ^ (s << 6), kq for s = 0
+  const int kq = l16 * 256 + ((g ^ l16) << 4);
+  // V^T A-operand (transpose read r of chunk ch, dim tile dt): row
+  // 32ch + 16r + q with q = 4g + l16 / 4, dims 16dt + 4(l16 % 4)
+  //   = (32ch + 16r) * 256 + (vq ^ (dt << 5))
+  const int vq_row = 4 * g + (l16 >> 2);
+  const int vq = vq_row * 256 + (((((l16 & 3) >> 1)) ^ vq_row) << 4) + 8 * (l16 & 1);
+  // DMA: instruction i of this wave covers rows 16 wave + 4i .. + 3; lane
+  // lands in row 16 wave + 4i + lane / 16 at physical column lane % 16
+  const int dr = lane >> 4, dc = lane & 15;
+  const char* kpool = static_cast<const char*>(p.k.data);
+  const char* vpool = static_cast<const char*>(p.v.data);
+  const uint32_t kts = (uint32_t)p.k.token_stride * 2, vts = (uint32_t)p.v.token_stride * 2;
+  const size_t khead = (size_t)h * p.k.head_stride * 2, vhead = (size_t)h * p.v.head_stride * 2;
+  const size_t kps = (size_t)p.k.page_stride * 2, vps = (size_t)p.v.page_stride * 2;
+  // byte offsets (within a tile) of the pieces this lane fetches
+  constexpr int kRowsPerWave = kBlock / kP3Waves;      // tile rows each wave fetches
+  constexpr int kDmaPerWave = kRowsPerWave / 4;         // 4 rows per DMA instruction
+  uint32_t koff[kDmaPerWave], voff[kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int row = kRowsPerWave * wave + 4 * i + dr;
+    const uint32_t col = (dc ^ (row & 15)) << 4;
+    koff[i] = row * kts + col;
+    voff[i] = row * vts + col;
+  }
+
+  auto stage = [&](int pg, int buf) {
+    if (pg < 0) pg = 0;
+    const char* kb = kpool + (size_t)pg * kps + khead;
+    const char* vb = vpool + (size_t)pg * vps + vhead;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      dma16(kb + koff[i], L.k[buf] + (kRowsPerWave * wave + 4 * i) * 256);
+      dma16(vb + voff[i], L.v[buf] + (kRowsPerWave * wave + 4 * i) * 256);
+    }
+  };
+
+  auto ring_fill = [&](int first) {
+    if (tid < kRingHalf) {
+      const int i = first + tid;
+      if (i < cnt) {
+        const int si = i & (2 * kRingHalf - 1);
+        L.ring_blk[si] = ids[i];
+        L.ring_pg[si] = pgs[i];
+        L.ring_msk[si] = msks[i];
+      }
+    }
+  };
+  ring_fill(0);
+  ring_fill(kRingHalf);
+  __syncthreads();
+  if (cnt > 0) stage(L.ring_pg[0], 0);
+
+  for (int e = 0; e < cnt; ++e) {
+    const int buf = e & 1;
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's DMA into buf has landed
+    __syncthreads();                   // ... and every other wave's
+    if (e >= kRingHalf && (e & (kRingHalf - 1)) == 0) ring_fill(e + kRingHalf);
+    const int rc = e & (2 * kRingHalf - 1);
+    const int blk = uniform(L.ring_blk[rc]);
+    const uint32_t msk = uniform(L.ring_msk[rc]);
+    // V rows past every token of the tile hold no data: zero them (only the
+    // tile's last block can have such rows) so that a zero probability never
+    // meets a NaN
+    if (blk * kBlock + kBlock - 1 > p_tile_max) {
+      for (int i = tid; i < kBlock * 16; i += kP3Waves * 64) {
+        const int row = i >> 4;
+        if (blk * kBlock + row > p_tile_max)
+          *reinterpret_cast<u32x4*>(L.v[buf] + row * 256 + (i & 15) * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (e + 1 < cnt) stage(L.ring_pg[(e + 1) & (2 * kRingHalf - 1)], buf ^ 1);
+    if (!(msk & wave_bits)) continue;
+
+    const bool diag = blk * kBlock + kBlock - 1 > p_wave_min;
+    bool live[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) live[ct] = plim_col[ct] >= 0 && ((msk >> tl_col[ct]) & 1u);
+    const char* kt = L.k[buf];
+    const char* vtl = L.v[buf];
+
+    // S^T for the block: with few columns both halves are computed up front
+    // so that the second half's MFMAs can overlap the first half's softmax;
+    // with 64 columns one half at a time fits the register file.
+    constexpr int kHalves = NCT <= 1 ? 2 : 1;
+    f32x4 S[kHalves][4][NCT];
+    auto qk_half = [&](int hb, f32x4 (&Sh)[4][NCT]) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + (64 * hb + 16 * pt) * 256 + (kq ^ (s << 6)));
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            Sh[pt][ct] = mfma_bf16(a, qf[ct][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : Sh[pt][ct]);
+        }
+    };
+    if constexpr (kHalves == 2) {
+      qk_half(0, S[0]);
+      qk_half(1, S[1]);
+    }
+
+#pragma unroll(kHalves)
+    for (int hb = 0; hb < 2; ++hb) {
+      const int sh = kHalves == 2 ? hb : 0;
+      if constexpr (kHalves == 1) qk_half(hb, S[0]);
+      bool rescale = false;
+      float alpha[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if (diag) {
+          const int lim = (live[ct] ? plim_col[ct] : -1) - (blk * kBlock + 64 * hb + 4 * g);
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * pt + i > lim) S[sh][pt][ct][i] = neg_inf();
+        }
+        float hmax = neg_inf();
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          hmax = fmaxf(hmax, fmaxf(fmaxf(S[sh][pt][ct][0], S[sh][pt][ct][1]),
+                                   fmaxf(S[sh][pt][ct][2], S[sh][pt][ct][3])));
+        hmax = colgroup_max(hmax) * sc;
+        // lazy rescaling: the reference max only moves when a score would
+        // exceed it by more than 2^kLazy, so probabilities stay <= 2^kLazy
+        // and O (held in accumulator registers) is rarely rescaled
+        const bool move = live[ct] && hmax > m_run[ct] + kLazy;
+        const float m_new = move ? hmax : m_run[ct];
+        const float m_use = m_new == neg_inf() ? 0.f : m_new;
+        const float off = live[ct] ? m_use : __builtin_inff();
+        alpha[ct] = move ? fast_exp2(m_run[ct] - m_use) : 1.f;
+        rescale |= move;
+        float lsum = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e2 = fast_exp2(__builtin_fmaf(S[sh][pt][ct][i], sc, -off));
+            S[sh][pt][ct][i] = e2;
+            lsum += e2;
+          }
+        l_run[ct] = l_run[ct] * alpha[ct] + lsum;
+        m_run[ct] = m_new;
+      }
+      if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) O[dt][ct] *= alpha[ct];
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        u32x4 bp[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const f32x4 s0 = S[sh][2 * cc][ct], s1 = S[sh][2 * cc + 1][ct];
+          bp[ct] = u32x4{pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]), pack_bf16(s1[0], s1[1]),
+                         pack_bf16(s1[2], s1[3])};
+        }
+        const int chunk = 2 * hb + cc;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const char* base = vtl + (32 * chunk) * 256 + (vq ^ (dt << 5));
+          const u32x2 lo = lds_tr8(base);
+          const u32x2 hi = lds_tr8(base + 16 * 256);
+          const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = mfma_bf16(a, bp[ct], O[dt][ct]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue ------------------------------------------------------------
+  // O^T tile dt, row m = 4g + i of the C layout is dim 16dt + 4g + i
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float l_tot = colgroup_sum(l_run[ct]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (plim_col[ct] < 0) continue;
+    const int cg = wave * cpw + ct * 16 + l16;
+    uint16_t* op = p.out + ((size_t)(r0 + t0 + tl_col[ct]) * p.H_q + h * p.G + cg % p.G) * kDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o = O[dt][ct];
+      *reinterpret_cast<u32x2*>(op + 16 * dt) = u32x2{pack_bf16(o[0] * inv, o[1] * inv),
+                                                     pack_bf16(o[2] * inv, o[3] * inv)};
+    }
+  }
+}
+
+template <int NCT>
+__global__ __launch_bounds__(64 * kP3Waves) void attn_prefill3_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) PrefillLds3 lds;
+  __shared__ int item_s;
+  for (;;) {
+    const int k = take_item(p.sched, &item_s);
+    if (k < 0) break;
+    attn_prefill3_tile<NCT>(p, p.worklist[k], lds);
+  }
+}
+
+void prefill_tiling(int G, bool fp8, int* tq, int* nct) {
+  if (fp8) {   // staged kernel: 8 waves, 16 * nct columns each
+    *tq = G >= 16 ? 16 : 32;
+    *nct = *tq * G / kPrefillWaves > 16 ? 2 : 1;
+  } else {     // direct-load kernel: kP3Waves waves of at most 32 columns
+    *tq = std::min(32, kP3Waves * 32 / G);
+    const int cpw = *tq * G / kP3Waves;
+    *nct = cpw > 16 ? 2 : 1;
+  }
 }
 
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s) {
@@ -689,14 +993,16 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   int tq, nct;
-  prefill_tiling(p, &tq, &nct);
-  const dim3 grid((unsigned)p.nwg), block(64 * kPrefillWaves);
+  prefill_tiling(p.G, fp8, &tq, &nct);
+  const dim3 grid((unsigned)p.nwg);
   if (fp8) {
+    const dim3 block(64 * kPrefillWaves);
     if (nct == 2) hipLaunchKernelGGL((attn_prefill_kernel<true, 2>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_prefill_kernel<true, 1>), grid, block, 0, s, p);
   } else {
-    if (nct == 2) hipLaunchKernelGGL((attn_prefill_kernel<false, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill_kernel<false, 1>), grid, block, 0, s, p);
+    const dim3 block(64 * kP3Waves);
+    if (nct == 2) hipLaunchKernelGGL((attn_prefill3_kernel<2>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<1>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
