@@ -688,7 +688,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnParams p) {
 // dims 16dt + 4(j % 4), which yields for lane (m, g) the positions
 // 16r + 4g + k of dim 16dt + m -- exactly the P^T B-operand layout.
 // ---------------------------------------------------------------------------
-constexpr int kP3Waves = 8;
+constexpr int kP3Waves = 16;
 constexpr float kLazy = 8.f;   // log2 headroom before the running max moves
 
 struct PrefillLds3 {
@@ -853,7 +853,7 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     // S^T for the block: with few columns both halves are computed up front
     // so that the second half's MFMAs can overlap the first half's softmax;
     // with 64 columns one half at a time fits the register file.
-    constexpr int kHalves = NCT <= 1 ? 2 : 1;
+    constexpr int kHalves = kP3Waves >= 16 ? 1 : (NCT <= 1 ? 2 : 1);
     f32x4 S[kHalves][4][NCT];
     auto qk_half = [&](int hb, f32x4 (&Sh)[4][NCT]) {
 #pragma unroll
