@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
     ap.add_argument("--partitions", type=int, default=0, help="split-K partitions (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a kernel of known "
+                         "traffic, to scale FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -147,7 +150,7 @@ def cpu_baseline(inp, wl, prefill, seconds):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("msa_attention.hip", "msa_common.h"):
+    for f in ("msa_attention.hip", "msa_common.h", "msa_kernels.h"):
         h.update(open(os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -283,6 +286,13 @@ def main():
              if args.workload == "all" else [args.workload])
     for name in names:
         print(json.dumps(run(name, args)), flush=True)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        sys.stderr.write(f"copy calibration: {src.numel() * 4} bytes read and written\n")
 
 
 if __name__ == "__main__":

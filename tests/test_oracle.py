@@ -78,7 +78,10 @@ def make_problem(rng, new_lens, cache_lens, H_kv=2, G=2, H_ik=1, D=16, top_k=3,
 
 
 def logical(pb, pool, b, h, n):
-    return O.gather_rows(pool, pb.kv_lookup_table[b], h, n)
+    """Positions 0..n-1 of head h of sequence b, looked up one by one in the
+    page table (independently of the oracle's own gather)."""
+    rows = [pool[int(pb.kv_lookup_table[b][j // BLK]), h, j % BLK] for j in range(n)]
+    return np.stack(rows) if rows else np.zeros((0, pool.shape[-1]), pool.dtype)
 
 
 # ---------------------------------------------------------------------------
