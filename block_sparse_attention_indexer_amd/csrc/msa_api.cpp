@@ -151,14 +151,20 @@ AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int re
     pl.np = req_np;
     return pl;
   }
-  // CU fill: aim for about 8 resident waves per CU; keep at least two blocks
-  // per partition when the batch alone already gives a few waves per CU.
+  // CU fill.  Measured on the decode workloads: once the batch alone gives
+  // two streaming waves per CU, one partition is fastest (no partial writes,
+  // no combine launch); below that, split until about four waves per CU, but
+  // keep at least two blocks per partition when the batch already gives a
+  // few waves per CU.
   const int64_t base = (int64_t)rg.batch * H_kv * ntok_groups;
-  const int64_t target = (int64_t)cus * 8;
-  int64_t np = (target + base - 1) / std::max<int64_t>(1, base);
-  const int union_blocks = std::min<int64_t>(top_k * pl.tpw, max_blocks(rg));
-  const int min_per = base >= cus / 2 ? 2 : 1;
-  np = std::min<int64_t>(np, std::max(1, union_blocks / min_per));
+  int64_t np = 1;
+  if (base < (int64_t)cus * 2) {
+    const int64_t target = (int64_t)cus * 4;
+    np = (target + base - 1) / std::max<int64_t>(1, base);
+    const int union_blocks = std::min<int64_t>(top_k * pl.tpw, max_blocks(rg));
+    const int min_per = base >= cus / 2 ? 2 : 1;
+    np = std::min<int64_t>(np, std::max(1, union_blocks / min_per));
+  }
   pl.np = (int)std::max<int64_t>(1, std::min<int64_t>(np, kMaxPartitions));
   return pl;
 }
@@ -254,9 +260,9 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.nbmax > top_k) {
     hipError_t e;
+    int cus = 0;
+    if ((st = current_device(&cus)) != MSA_OK) return st;
     if (route_of(*rg) == Route::Prefill) {
-      int cus = 0;
-      if ((st = current_device(&cus)) != MSA_OK) return st;
       p.tq = prefill_indexer_tile(num_kv_heads, p.H_ik);
       p.ntiles = (rg->max_seq_length + p.tq - 1) / p.tq;
       const size_t stride = (size_t)p.score_stride;
@@ -266,7 +272,7 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
       p.worklist = reinterpret_cast<int32_t*>(w + align_up(2 * sizeof(int32_t)));
       e = launch_indexer_prefill(p, cus, s);
     } else {
-      e = launch_indexer_decode(p, s);
+      e = launch_indexer_decode(p, cus, s);
     }
     if (e != hipSuccess) return MSA_ERR_LAUNCH;
   }

@@ -12,109 +12,238 @@
 namespace msa {
 
 // ---------------------------------------------------------------------------
-// Block-max scorer, streaming index-K pages from HBM.
+// Block-max scorer for the decode and speculative routes, streaming index-K
+// pages from HBM.
 //
-// Workgroup = 4 waves; each wave scores kBpw consecutive blocks of one
-// sequence against up to 16 * NCT columns.  A column is one (token, KV head)
-// pair whose KV head reads index-K head hk (one shared head, or one per KV
-// head).  Per block the wave loads the 128 x 128 BF16 tile straight into
-// MFMA A-operand registers (16 B per lane per load, 64 B contiguous per row
-// per instruction), computes S^T = K Q^T with the columns on the MFMA N side,
-// then reduces rows (positions) with in-lane max plus two cross-lane steps.
+// Work unit = one 128 x 128 index-K tile scored against one column group: up
+// to 16 * NCT columns, a column being one (token, KV head) pair of a sequence
+// whose KV head reads index-K head hk (one shared head, or one per KV head).
+// Units are ordered (sequence, hk, column group, block) and split into equal
+// contiguous shares, one per wave of a grid sized to be resident at once, so
+// that every wave streams the same number of bytes whatever the mix of
+// context lengths.  Each workgroup recomputes the per-sequence unit counts
+// from the ragged metadata (a prefix over chunks of sequences in LDS) rather
+// than reading a plan written by another launch.
+//
+// A wave walks its share in segments that stay inside one column group.  Per
+// segment it loads the page ids with one vector load and the query columns
+// into MFMA B operands, then streams the tiles as 64-position halves straight
+// into A-operand registers (16 B per lane per load, 64 B contiguous per row
+// per instruction) with the next half in flight while the current one is
+// multiplied.  S^T = K Q^T puts the columns on the MFMA N side; rows
+// (positions) reduce with an in-lane max plus two cross-lane steps.
 // ---------------------------------------------------------------------------
 constexpr int kIdxWaves = 4;
-constexpr int kBpw = 2;
+constexpr int kIdxThreads = 64 * kIdxWaves;
+constexpr int kMaxSegment = 64;   // blocks per segment: one page id per lane
+
+// Blocks [lo, hi) that column group cg of a sequence with n new tokens and c
+// cached ones must score; empty when none of its rows needs a score.
+struct GroupRange {
+  int lo, hi;
+};
 
 template <int NCT>
-__global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int b = blockIdx.y;
-  const int hk = blockIdx.z % p.H_ik;
-  const int cg = blockIdx.z / p.H_ik;
-  const int r0 = p.rg.offs[b];
-  // Rows past the host bound never exist; the clamp keeps every address in
-  // the buffers sized from the bounds.
-  const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
-  const int hpi = p.H_kv / p.H_ik;          // KV heads per index-K head
-  const int col0 = cg * 16 * NCT;           // first column of this group
-  if (n <= 0 || col0 >= n * hpi) return;
-  const int c = p.rg.clen[b];
-  // Tokens of this column group and the blocks any of them may need scored.
+__device__ __forceinline__ GroupRange group_range(const IndexerParams& p, int n, int c, int hpi, int cg) {
+  const int col0 = cg * 16 * NCT;
+  GroupRange r{0, 0};
+  if (col0 >= n * hpi) return r;
   const int t_last = min(n, (col0 + 16 * NCT + hpi - 1) / hpi) - 1;
   const int nb_last = (c + t_last) / kBlock + 1;
-  if (nb_last <= p.top_k) return;           // every row selects all its blocks
-  const int blk_hi = min(nb_last - p.local, p.nbmax);
+  if (nb_last <= p.top_k) return r;          // every row selects all its blocks
+  r.lo = p.init;
+  r.hi = max(r.lo, min(nb_last - p.local, p.nbmax));
+  return r;
+}
 
-  u32x4 qf[NCT][4];
-  int plim[NCT];     // last visible position of the column's token (-1: none)
-  int orow[NCT];     // (row, KV head) index of the column
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int cc = col0 + ct * 16 + l16;
-    const int t = cc / hpi;
-    const int h = hk + p.H_ik * (cc % hpi);
-    const bool ok = t < n;
-    plim[ct] = ok ? c + t : -1;
-    orow[ct] = ok ? (r0 + t) * p.H_kv + h : 0;
-    const uint16_t* qp = p.q_idx + (size_t)orow[ct] * kDim;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[ct][s] = ok ? ld16(qp + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+// New tokens (clamped to the host bound, so that every address stays inside
+// buffers sized from it) and cached tokens of sequence b.
+__device__ __forceinline__ int2 seq_shape(const IndexerParams& p, int b) {
+  const int r0 = p.rg.offs[b];
+  const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
+  return int2{max(n, 0), p.rg.clen[b]};
+}
+
+template <int NCT>
+__device__ __forceinline__ int64_t group_units(const IndexerParams& p, int n, int c, int hpi, int ncg) {
+  int64_t u = 0;
+  for (int cg = 0; cg < ncg; ++cg) {
+    const GroupRange r = group_range<NCT>(p, n, c, hpi, cg);
+    u += r.hi - r.lo;
   }
+  return u;
+}
 
-  const int blk0 = (blockIdx.x * kIdxWaves + wave) * kBpw;
-  const uint16_t* pool = static_cast<const uint16_t*>(p.ik.data);
-  for (int bi = 0; bi < kBpw; ++bi) {
-    const int blk = blk0 + bi;
-    if (blk < p.init || blk >= blk_hi) continue;
-    const int page = uniform(p.rg.table[(size_t)b * p.rg.stride + blk]);
-    if ((unsigned)page >= (unsigned)p.ik.num_pages) continue;
-    const uint16_t* base = pool + (size_t)page * p.ik.page_stride + (size_t)hk * p.ik.head_stride;
-    u32x4 kf[8][4];
-#pragma unroll
-    for (int pt = 0; pt < 8; ++pt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kf[pt][s] = ld16(base + (size_t)(16 * pt + l16) * p.ik.token_stride + 32 * s + 8 * g);
+template <int NCT>
+__global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParams p, int ncg) {
+  __shared__ int64_t chunk_pre[kIdxThreads + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform((int)(threadIdx.x >> 6));
+  const int l16 = lane & 15, g = lane >> 4;
+  const int B = p.rg.batch;
+  const int hpi = p.H_kv / p.H_ik;           // KV heads per index-K head
+  const int cpt = (B + kIdxThreads - 1) / kIdxThreads;   // sequences per chunk
 
-    const bool clip = blk * kBlock + kBlock - 1 > c;   // some position past a token
-    float mx[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) mx[ct] = neg_inf();
-#pragma unroll
-    for (int pt = 0; pt < 8; ++pt) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_bf16(kf[pt][s], qf[ct][s], acc);
-        if (clip) {
-          const int pos0 = blk * kBlock + 16 * pt + 4 * g;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (pos0 + i > plim[ct]) acc[i] = neg_inf();
-        }
-        mx[ct] = fmaxf(mx[ct], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-      }
+  // units of each chunk of cpt sequences, then an inclusive scan over chunks
+  {
+    int64_t u = 0;
+    const int b_end = min(B, (int)(threadIdx.x + 1) * cpt);
+    for (int b = threadIdx.x * cpt; b < b_end; ++b) {
+      const int2 nc = seq_shape(p, b);
+      if (nc.x > 0) u += group_units<NCT>(p, nc.x, nc.y, hpi, ncg) * p.H_ik;
     }
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t v = __shfl_up(u, d);
+      if (lane >= d) u += v;
+    }
+    chunk_pre[threadIdx.x + 1] = u;
+    __syncthreads();
+    int64_t add = 0;
+    for (int w = 0; w < wave; ++w) add += chunk_pre[64 * w + 64];
+    __syncthreads();
+    chunk_pre[threadIdx.x + 1] = u + add;
+    if (threadIdx.x == 0) chunk_pre[0] = 0;
+    __syncthreads();
+  }
+  const int64_t total = chunk_pre[kIdxThreads];
+  const int64_t W = (int64_t)gridDim.x * kIdxWaves;
+  const int64_t w = (int64_t)blockIdx.x * kIdxWaves + wave;
+  const int64_t base = total / W, rem = total % W;
+  int64_t s = w * base + min(w, rem);
+  const int64_t e = s + base + (w < rem ? 1 : 0);
+
+  const char* pool = static_cast<const char*>(p.ik.data);
+  const size_t ts = (size_t)p.ik.token_stride * 2;
+  const size_t ps = (size_t)p.ik.page_stride * 2;
+  const size_t lane_off = (size_t)l16 * ts + (8 * g) * 2;
+
+  while (s < e) {
+    // chunk holding unit s: the last j with chunk_pre[j] <= s
+    int lo = 0, hi = kIdxThreads;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (chunk_pre[mid] <= s) lo = mid; else hi = mid;
+    }
+    // walk the chunk's sequences, then (hk, column group) inside the sequence
+    int64_t acc = chunk_pre[lo];
+    int b = lo * cpt;
+    int2 nc = seq_shape(p, b);
+    int64_t per_hk = nc.x > 0 ? group_units<NCT>(p, nc.x, nc.y, hpi, ncg) : 0;
+    while (acc + per_hk * p.H_ik <= s) {
+      acc += per_hk * p.H_ik;
+      ++b;
+      nc = seq_shape(p, b);
+      per_hk = nc.x > 0 ? group_units<NCT>(p, nc.x, nc.y, hpi, ncg) : 0;
+    }
+    const int n = nc.x, c = nc.y;
+    int64_t o = s - acc;
+    const int hk = (int)(o / per_hk);
+    o -= (int64_t)hk * per_hk;
+    int cg = 0;
+    GroupRange gr = group_range<NCT>(p, n, c, hpi, 0);
+    while (o >= gr.hi - gr.lo) {
+      o -= gr.hi - gr.lo;
+      ++cg;
+      gr = group_range<NCT>(p, n, c, hpi, cg);
+    }
+    const int blk_lo = gr.lo + (int)o;
+    const int nblk = (int)min(min((int64_t)(gr.hi - blk_lo), e - s), (int64_t)kMaxSegment);
+    s += nblk;
+
+    const int r0 = p.rg.offs[b];
+    const int col0 = cg * 16 * NCT;
+    u32x4 qf[NCT][4];
+    int plim[NCT];     // last visible position of the column's token (-1: none)
+    int orow[NCT];     // (row, KV head) index of the column
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float m = colgroup_max(mx[ct]);
-      if (g == 0 && plim[ct] >= 0) p.scores[(size_t)orow[ct] * p.score_stride + blk] = m;
+      const int cc = col0 + ct * 16 + l16;
+      const int t = cc / hpi;
+      const int h = hk + p.H_ik * (cc % hpi);
+      const bool ok = t < n;
+      plim[ct] = ok ? c + t : -1;
+      orow[ct] = ok ? (r0 + t) * p.H_kv + h : 0;
+      const uint16_t* qp = p.q_idx + (size_t)orow[ct] * kDim;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) qf[ct][q] = ok ? ld16(qp + 32 * q + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // page ids of the segment's blocks, one per lane; out-of-pool ids read
+    // page 0 and write no score
+    int pg_lane = 0;
+    if (lane < nblk) pg_lane = p.rg.table[(size_t)b * p.rg.stride + blk_lo + lane];
+    if ((unsigned)pg_lane >= (unsigned)p.ik.num_pages) pg_lane = -1;
+    const char* head_base = pool + (size_t)hk * p.ik.head_stride * 2 + lane_off;
+
+    auto load_half = [&](int u, u32x4 (&kf)[4][4]) {
+      int pg = __builtin_amdgcn_readlane(pg_lane, u >> 1);
+      if (pg < 0) pg = 0;
+      const char* src = head_base + (size_t)pg * ps + (size_t)(64 * (u & 1)) * ts;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kf[pt][q] = ld16(src + (size_t)(16 * pt) * ts + 64 * q);
+    };
+
+    float mx[NCT];
+    auto compute_half = [&](int u, const u32x4 (&kf)[4][4]) {
+      const int blk = blk_lo + (u >> 1);
+      const int pos_base = blk * kBlock + 64 * (u & 1);
+      const bool clip = pos_base + 63 > c;   // some position past a token
+      if ((u & 1) == 0) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) mx[ct] = neg_inf();
+      }
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc4 = mfma_bf16(kf[pt][q], qf[ct][q], acc4);
+          if (clip) {
+            const int lim = plim[ct] - (pos_base + 16 * pt + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i > lim) acc4[i] = neg_inf();
+          }
+          mx[ct] = fmaxf(mx[ct], fmaxf(fmaxf(acc4[0], acc4[1]), fmaxf(acc4[2], acc4[3])));
+        }
+      }
+      if (u & 1) {
+        const bool page_ok = __builtin_amdgcn_readlane(pg_lane, u >> 1) >= 0;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const float m = colgroup_max(mx[ct]);
+          if (page_ok && g == 0 && plim[ct] >= 0) p.scores[(size_t)orow[ct] * p.score_stride + blk] = m;
+        }
+      }
+    };
+
+    // halves 0 .. 2 nblk - 1 with the next one always in flight
+    u32x4 kA[4][4], kB[4][4];
+    load_half(0, kA);
+    for (int j = 0; j < nblk; ++j) {
+      load_half(2 * j + 1, kB);
+      compute_half(2 * j, kA);
+      if (j + 1 < nblk) load_half(2 * j + 2, kA);
+      compute_half(2 * j + 1, kB);
     }
   }
 }
 
-hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
+// Waves the scorer keeps resident per CU (register-limited occupancy).
+constexpr int score_waves_per_cu(int nct) { return nct >= 4 ? 4 : 8; }
+
+hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_t s) {
   const int hpi = p.H_kv / p.H_ik;
   const int cols = p.rg.max_seq * hpi;
   const int nct = cols <= 16 ? 1 : cols <= 32 ? 2 : 4;
   const int ncg = (cols + 16 * nct - 1) / (16 * nct);
-  dim3 grid((p.nbmax + kIdxWaves * kBpw - 1) / (kIdxWaves * kBpw), p.rg.batch, p.H_ik * ncg);
-  if (nct == 1) hipLaunchKernelGGL(indexer_score_kernel<1>, grid, dim3(256), 0, s, p);
-  else if (nct == 2) hipLaunchKernelGGL(indexer_score_kernel<2>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(indexer_score_kernel<4>, grid, dim3(256), 0, s, p);
+  dim3 grid(num_cus * score_waves_per_cu(nct) / kIdxWaves);
+  if (nct == 1) hipLaunchKernelGGL(indexer_score_kernel<1>, grid, dim3(kIdxThreads), 0, s, p, ncg);
+  else if (nct == 2) hipLaunchKernelGGL(indexer_score_kernel<2>, grid, dim3(kIdxThreads), 0, s, p, ncg);
+  else hipLaunchKernelGGL(indexer_score_kernel<4>, grid, dim3(kIdxThreads), 0, s, p, ncg);
   return hipGetLastError();
 }
 
@@ -133,7 +262,7 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform((int)(threadIdx.x >> 6));
   const int b = blockIdx.y;
   const int idx = blockIdx.x * 4 + wave;
   const int t = idx / p.H_kv;
@@ -157,12 +286,14 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
 
   const float* sc = p.scores + ((size_t)r * p.H_kv + h) * p.score_stride + p.init;
   const int nslot = (ncand + 63) / 64;
+  // Every slot loads (clamped into the candidate range) so that all loads are
+  // in flight together; keys past the candidates are 0, below every real key.
+  float v[KPL];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) v[s] = sc[min(s * 64 + lane, ncand - 1)];
   uint32_t key[KPL];
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    const int i = s * 64 + lane;
-    key[s] = (s < nslot && i < ncand) ? score_key(sc[i]) : 0u;
-  }
+  for (int s = 0; s < KPL; ++s) key[s] = s * 64 + lane < ncand ? score_key(v[s]) : 0u;
   uint32_t thr = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);

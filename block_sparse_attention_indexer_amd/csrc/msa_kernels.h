@@ -75,7 +75,7 @@ struct CombineParams {
 };
 
 // Launchers; each returns hipSuccess or the launch error.
-hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
+hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_t s);
 hipError_t launch_indexer_prefill(const IndexerParams& p, int num_cus, hipStream_t s);
 int prefill_indexer_tile(int H_kv, int H_ik);
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s);

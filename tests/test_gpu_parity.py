@@ -117,6 +117,27 @@ def test_explicit_partitions(np_):
     run_and_check(wl_custom(f"np{np_}", [1, 2, 5], [8000, 3000, 255], top_k=9), num_partitions=np_)
 
 
+def test_split_k_at_full_size():
+    # the automatic plan keeps these batches in one partition; force a split
+    run_and_check(I.decode_batch64(), seqs=[2, 33, 63], num_partitions=4)
+    run_and_check(I.spec_decode(), seqs=[1, 30], num_partitions=3)
+
+
+def test_many_sequences_per_scorer_chunk():
+    # more sequences than scorer threads: each prefix chunk spans several
+    rng = np.random.default_rng(11)
+    n = 300
+    cached = rng.integers(300, 3000, size=n)
+    new = rng.integers(0, 3, size=n)
+    wl = wl_custom("b300", new.tolist(), cached.tolist(), top_k=4, seed=11)
+    run_and_check(wl, seqs=[0, 1, 2, 255, 256, 257, 298, 299])
+
+
+def test_two_column_groups_per_sequence():
+    # 16 KV heads sharing one index head x 8 draft tokens = 128 columns
+    run_and_check(wl_custom("cg2", [8, 3, 6], [3000, 5000, 700], H_kv=16, G=1, top_k=5))
+
+
 def test_tie_break_lower_id_on_all_equal_scores():
     wl = wl_custom("ties", [1, 2], [20 * 128 + 3, 9 * 128], top_k=6, init=1, local=2)
     inp = I.make_inputs(wl, DEV)
