@@ -57,6 +57,12 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a kernel of known "
                          "traffic, to scale FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="instead of timing: turn the rocprofv3 counter_collection.csv files of a "
+                         "FETCH_SIZE run and a WRITE_SIZE run (both with --copy-calibration) into "
+                         "the attention kernel's HBM traffic record for --workload")
+    ap.add_argument("--traffic-out", default=None,
+                    help="where --traffic-record writes its JSON (default: stdout)")
     return ap.parse_args()
 
 
@@ -165,6 +171,90 @@ def traffic_record(workload):
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30     # the --copy-calibration copy reads and writes 1 GiB
+
+
+def _counter_per_dispatch(path, counter):
+    """{kernel name: [counter value per dispatch]} from a counter_collection.csv
+    (rows of one dispatch are summed over the instances they are reported for)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def write_traffic_record(args):
+    """HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what the same counters read for the 1 GiB
+    calibration copy, next to the algorithmic gathered-KV bytes of the launch."""
+    import torch
+
+    from block_sparse_attention_indexer_amd import binding as B
+    from block_sparse_attention_indexer_amd import inputs as I
+
+    fetch_csv, write_csv = args.traffic_record
+    scaled = {}
+    raw = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = _counter_per_dispatch(path, counter)
+        copy = max(v for name, vals in per.items() if "copy" in name.lower() for v in vals)
+        attn = [v for name, vals in per.items() if "attn_decode_kernel" in name for v in vals]
+        if not attn:
+            raise SystemExit(f"no attn_decode_kernel dispatch in {path}")
+        scale = COPY_BYTES / (copy * 1024.0)
+        raw[counter] = (float(np.mean(attn)), copy, scale, len(attn))
+        scaled[counter] = float(np.mean(attn)) * 1024.0 * scale
+
+    wl = I.WORKLOADS[args.workload]()
+    inp = I.make_inputs(wl, "cuda")
+    d = B.run_indexer(inp)
+    torch.cuda.synchronize()
+    algo = algorithmic_work(wl, d.cpu().numpy())["kv_bytes"]
+    hbm = scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"]
+    cmd = ("rocprofv3 --pmc {c} --kernel-include-regex 'attn_decode_kernel|copy|elementwise' "
+           "--output-format csv -d $R/gpurun_out/pmc_{w}_{l} -o run -- python3 $R/bench.py "
+           "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration")
+    rec = {
+        "kernel": "msa::attn_decode_kernel",
+        "workload": f"{args.workload} ({wl.name})",
+        "fetch_size_kib_per_launch": raw["FETCH_SIZE"][0],
+        "write_size_kib_per_launch": raw["WRITE_SIZE"][0],
+        "dispatches_averaged": raw["FETCH_SIZE"][3],
+        "calibration": {
+            "fetch_scale": raw["FETCH_SIZE"][2], "write_scale": raw["WRITE_SIZE"][2],
+            "how": (f"the same runs include one plain 1 GiB device-to-device copy (bench.py "
+                    f"--copy-calibration): FETCH_SIZE reads {raw['FETCH_SIZE'][1]:.0f} KiB and "
+                    f"WRITE_SIZE {raw['WRITE_SIZE'][1]:.0f} KiB for 1048576 KiB moved each way"),
+        },
+        "hbm_bytes_per_launch": int(round(hbm)),
+        "algorithmic_gathered_kv_bytes_per_launch": int(algo),
+        "hbm_over_algorithmic": hbm / algo if algo else None,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "commands": [cmd.format(c="FETCH_SIZE", w=args.workload, l="fetch"),
+                     cmd.format(c="WRITE_SIZE", w=args.workload, l="write"),
+                     f"python3 $R/bench.py --workload {args.workload} --traffic-record "
+                     f"$R/gpurun_out/pmc_{args.workload}_fetch/run_counter_collection.csv "
+                     f"$R/gpurun_out/pmc_{args.workload}_write/run_counter_collection.csv"],
+        "note": ("counter runs on the GPU box from /tmp with TMPDIR=/tmp; $R is the repository "
+                 "root. HBM bytes beyond the algorithmic gathered-KV bytes are q, the block ids, "
+                 "page-table entries, the output (and split-K partials when the row is split), "
+                 "the unused rows of partly filled blocks and blocks that several token groups "
+                 "of one sequence load separately."),
+    }
+    text = json.dumps(rec, indent=2) + "\n"
+    if args.traffic_out:
+        open(args.traffic_out, "w").write(text)
+    else:
+        sys.stdout.write(text)
 
 
 def run(workload, args):
@@ -282,6 +372,9 @@ def main():
         sys.stderr.write("bench.py needs a GPU\n")
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.traffic_record:
+        write_traffic_record(args)
+        return
     names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long"]
              if args.workload == "all" else [args.workload])
     for name in names:

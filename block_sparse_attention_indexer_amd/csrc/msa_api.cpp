@@ -87,6 +87,8 @@ int check_cache(const msa_paged_cache* c, bool allow_fp8) {
   for (int64_t st : {c->page_stride, c->head_stride, c->token_stride})
     if (st < 0 || (st * esz) % 16) return MSA_ERR_SHAPE;
   if (c->token_stride < MSA_HEAD_DIM) return MSA_ERR_SHAPE;
+  // kernels address the rows of one page with 32-bit byte offsets
+  if (c->token_stride * esz * MSA_BLOCK_SIZE > (int64_t)INT32_MAX) return MSA_ERR_SHAPE;
   return MSA_OK;
 }
 

@@ -20,6 +20,8 @@
 // so the softmax statistics of a column stay in the lanes that own it and
 // no LDS round trip is needed.  Online softmax runs per 64-position half
 // block in log2 units.
+#include <type_traits>
+
 #include "msa_common.h"
 #include "msa_kernels.h"
 
@@ -127,67 +129,85 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   const char* kpool = static_cast<const char*>(p.k.data);
   const char* vpool = static_cast<const char*>(p.v.data);
   const size_t kts = (size_t)p.k.token_stride * esz, vts = (size_t)p.v.token_stride * esz;
+  const size_t khead = (size_t)h * p.k.head_stride * esz, vhead = (size_t)h * p.v.head_stride * esz;
+  const size_t kps = (size_t)p.k.page_stride * esz, vps = (size_t)p.v.page_stride * esz;
+  // per-lane byte offsets inside a half block; a page's rows span less than
+  // 2 GiB (checked on the host), so 32 bits hold them
+  const uint32_t koff = (uint32_t)l16 * (uint32_t)kts + (FP8 ? 32u : 16u) * g;
+  const uint32_t voff = (uint32_t)(4 * g) * (uint32_t)vts + (FP8 ? 8u : 16u) * l16;
 
-  for (int e = e_lo; e < e_hi; ++e) {
-    const int blk = uniform(uid[e]);
-    const uint32_t msk = uniform(umk[e]);
-    const int page = uniform(p.rg.table[(size_t)b * p.rg.stride + blk]);
-    if ((unsigned)page >= (unsigned)p.k.num_pages) continue;
-    const int plim = (col_ok && ((msk >> tl_col) & 1u)) ? p_col : -1;
-    const char* kb = kpool + ((size_t)page * p.k.page_stride + (size_t)h * p.k.head_stride) * esz;
-    const char* vb = vpool + ((size_t)page * p.v.page_stride + (size_t)h * p.v.head_stride) * esz;
+  // Raw tiles of one 64-position half block.  BF16: K as MFMA A operands
+  // (4 position tiles x 4 k-steps), V as 2 chunks x 8 rows of 8 dims per
+  // lane.  FP8: the same bytes at half width, widened when consumed.
+  constexpr int KW = FP8 ? 2 : 4;
+  typedef typename std::conditional<FP8, u32x2, u32x4>::type VRaw;
+  u32x4 kraw[4][KW];
+  VRaw vraw[2][8];
 
-#pragma unroll 1
-    for (int hb = 0; hb < 2; ++hb) {
-      const int rb = 64 * hb;
-      const int pos0 = blk * kBlock + rb;
-      // -- loads: K (4 position tiles) and V (2 chunks x 8 rows) ----------
-      u32x4 kf[4][4];
-      u32x4 vrow[2][8];
-      if constexpr (!FP8) {
+  // The slice is walked in segments of up to 64 union entries; per segment
+  // each lane holds one entry's block id, token mask and page id, so that no
+  // table lookup sits between consecutive blocks.  Inside a segment the
+  // halves form a pipeline: K of the next half is requested as soon as the
+  // scores of the current half have consumed K, V of the next half as soon
+  // as P V has consumed V, so one half's worth of loads is always in flight.
+  const int nE = e_hi - e_lo;
+  for (int s0 = 0; s0 < nE; s0 += 64) {
+    const int nS = min(64, nE - s0);
+    int blk_lane = 0, pg_lane = -1;
+    uint32_t mk_lane = 0u;
+    if (lane < nS) {
+      blk_lane = uid[e_lo + s0 + lane];
+      mk_lane = umk[e_lo + s0 + lane];
+      const int pg = p.rg.table[(size_t)b * p.rg.stride + blk_lane];
+      pg_lane = (unsigned)pg < (unsigned)p.k.num_pages ? pg : -1;   // bad ids: block skipped
+    }
+
+    // Addresses = wave-uniform base (page, head, half block, row constant)
+    // + a 32-bit per-lane offset, so the loads take the scalar-base form.
+    auto page_of = [&](int u) { return max(__builtin_amdgcn_readlane(pg_lane, u >> 1), 0); };
+    auto issue_k = [&](int u) {
+      const char* kb = kpool + (size_t)page_of(u) * kps + khead + (size_t)(64 * (u & 1)) * kts;
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < 4; ++pt) {
+        const char* rowb = kb + (size_t)(16 * pt) * kts;
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            kf[pt][s] = ld16(kb + (rb + 16 * pt + l16) * kts + (32 * s + 8 * g) * 2);
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            vrow[ch][j] = ld16(vb + (rb + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3)) * vts + 16 * l16);
-      } else {
-        u32x4 kr[4][2];
-        u32x2 vr[2][8];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          kr[pt][0] = ld16(kb + (rb + 16 * pt + l16) * kts + 32 * g);
-          kr[pt][1] = ld16(kb + (rb + 16 * pt + l16) * kts + 32 * g + 16);
-        }
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            vr[ch][j] = ld8(vb + (rb + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3)) * vts + 8 * l16);
-        if (pos0 + 63 > p_max) {
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (pos0 + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3) > p_max) vr[ch][j] = u32x2{0u, 0u};
-        }
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const u32x4 w = kr[pt][s >> 1];
-            kf[pt][s] = fp8x8_to_bf16x8((s & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y});
-          }
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vrow[ch][j] = fp8x8_to_bf16x8(vr[ch][j]);
+        for (int s = 0; s < KW; ++s) kraw[pt][s] = ld16(rowb + koff + (FP8 ? 16 * s : 64 * s));
       }
-      // -- S^T = K Q^T -----------------------------------------------------
+    };
+    auto issue_v = [&](int u) {
+      const char* vb = vpool + (size_t)page_of(u) * vps + vhead + (size_t)(64 * (u & 1)) * vts;
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const char* rowb = vb + (size_t)(32 * ch + 16 * (j >> 2) + (j & 3)) * vts;
+          if constexpr (FP8) vraw[ch][j] = ld8(rowb + voff);
+          else vraw[ch][j] = ld16(rowb + voff);
+        }
+    };
+
+    auto half = [&](int u, auto prefetch) {
+      constexpr bool kNext = decltype(prefetch)::value;
+      const int i = u >> 1;
+      const int blk = __builtin_amdgcn_readlane(blk_lane, i);
+      const uint32_t msk = __builtin_amdgcn_readlane(mk_lane, i);
+      const bool pvalid = __builtin_amdgcn_readlane(pg_lane, i) >= 0;
+      const int plim = (pvalid && col_ok && ((msk >> tl_col) & 1u)) ? p_col : -1;
+      const int pos0 = blk * kBlock + 64 * (u & 1);
+
+      // -- S^T = K Q^T ------------------------------------------------------
+      u32x4 kf[4][4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (FP8) {
+            const u32x4 w = kraw[pt][s >> 1];
+            kf[pt][s] = fp8x8_to_bf16x8((s & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y});
+          } else {
+            kf[pt][s] = kraw[pt][s];
+          }
+        }
       f32x4 sacc[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
@@ -195,15 +215,21 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) sacc[pt] = mfma_bf16(kf[pt][s], qf[s], sacc[pt]);
       }
+      // fences keep the next half's loads from being hoisted above the
+      // instructions that still read the buffers they overwrite
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kNext) issue_k(u + 1);
+      __builtin_amdgcn_sched_barrier(0);
+
       // -- scale, causal/selection mask, online softmax ---------------------
       float hmax = neg_inf();
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = pos0 + 16 * pt + 4 * g + i;
-          const float v = pos <= plim ? sacc[pt][i] * p.scale_log2 : neg_inf();
-          sacc[pt][i] = v;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int pos = pos0 + 16 * pt + 4 * g + ii;
+          const float v = pos <= plim ? sacc[pt][ii] * p.scale_log2 : neg_inf();
+          sacc[pt][ii] = v;
           hmax = fmaxf(hmax, v);
         }
       hmax = colgroup_max(hmax);
@@ -214,32 +240,42 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e2 = exp2f(sacc[pt][i] - m_use);
-          sacc[pt][i] = e2;
+        for (int ii = 0; ii < 4; ++ii) {
+          const float e2 = exp2f(sacc[pt][ii] - m_use);
+          sacc[pt][ii] = e2;
           lsum += e2;
         }
       l_run = l_run * alpha + lsum;
       m_run = m_new;
 #pragma unroll
       for (int T = 0; T < 8; ++T) O[T] *= alpha;
-      // -- V rows past every token of the wave hold no data: zero them ------
-      if constexpr (!FP8) {
-        if (pos0 + 63 > p_max) {
+
+      // -- V rows past every token of the wave (or of a skipped block) hold
+      //    no data: zero them so that 0 * garbage cannot poison O ---------
+      if (!pvalid || pos0 + 63 > p_max) {
 #pragma unroll
-          for (int ch = 0; ch < 2; ++ch)
+        for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (pos0 + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3) > p_max)
-                vrow[ch][j] = u32x4{0u, 0u, 0u, 0u};
-        }
+          for (int j = 0; j < 8; ++j)
+            if (!pvalid || pos0 + 32 * ch + 16 * (j >> 2) + 4 * g + (j & 3) > p_max) vraw[ch][j] = VRaw{};
       }
+      u32x4 vrow[2][8];
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (FP8) vrow[ch][j] = fp8x8_to_bf16x8(vraw[ch][j]);
+          else vrow[ch][j] = vraw[ch][j];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (FP8 && kNext) issue_v(u + 1);
+
       // -- O^T += V^T P^T ---------------------------------------------------
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        const f32x4 s0 = sacc[2 * ch], s1 = sacc[2 * ch + 1];
-        const u32x4 bp = {pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]),
-                          pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3])};
+        const f32x4 s0v = sacc[2 * ch], s1v = sacc[2 * ch + 1];
+        const u32x4 bp = {pack_bf16(s0v[0], s0v[1]), pack_bf16(s0v[2], s0v[3]),
+                          pack_bf16(s1v[0], s1v[1]), pack_bf16(s1v[2], s1v[3])};
 #pragma unroll
         for (int T = 0; T < 8; ++T) {
           u32x4 a;
@@ -249,7 +285,16 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
           O[T] = mfma_bf16(a, bp, O[T]);
         }
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!FP8 && kNext) issue_v(u + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    issue_k(0);
+    issue_v(0);
+    const int nh = 2 * nS;
+    for (int u = 0; u < nh - 1; ++u) half(u, std::true_type{});
+    half(nh - 1, std::false_type{});
   }
 
   // ---- epilogue: normalise and store --------------------------------------

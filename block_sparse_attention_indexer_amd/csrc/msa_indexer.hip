@@ -286,11 +286,15 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
 
   const float* sc = p.scores + ((size_t)r * p.H_kv + h) * p.score_stride + p.init;
   const int nslot = (ncand + 63) / 64;
-  // Every slot loads (clamped into the candidate range) so that all loads are
-  // in flight together; keys past the candidates are 0, below every real key.
+  // Slots holding candidates load (lanes past the end read the last one) with
+  // no use between the loads, so that they are all in flight together; keys
+  // past the candidates are 0, below every real key.
   float v[KPL];
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) v[s] = sc[min(s * 64 + lane, ncand - 1)];
+  for (int s = 0; s < KPL; ++s) v[s] = 0.f;
+#pragma unroll
+  for (int s = 0; s < KPL; ++s)
+    if (s < nslot) v[s] = sc[min(s * 64 + lane, ncand - 1)];
   uint32_t key[KPL];
 #pragma unroll
   for (int s = 0; s < KPL; ++s) key[s] = s * 64 + lane < ncand ? score_key(v[s]) : 0u;

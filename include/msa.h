@@ -107,7 +107,9 @@ typedef struct msa_paged_cache {
     int32_t reserved;        /* set to 0                                          */
     int64_t page_stride;     /* elements between pages                            */
     int64_t head_stride;     /* elements between heads of one page                */
-    int64_t token_stride;    /* elements between slots of one head                */
+    int64_t token_stride;    /* elements between slots of one head; >= 128, and   */
+                             /* the 128 slots of a page span < 2 GiB              */
+                             /* (token_stride * element size * 128 <= INT32_MAX)  */
 } msa_paged_cache;
 
 /* The ragged batch: which rows are whose, and where their KV lives. */

@@ -48,6 +48,7 @@ def test_indexer_validation():
     assert indexer(rg(), cache(heads=3)) == SHAPE
     assert indexer(rg(), cache(tok=100)) == SHAPE            # unaligned stride
     assert indexer(rg(), cache(data=FAKE + 2)) == SHAPE      # unaligned base
+    assert indexer(rg(), cache(tok=1 << 23)) == SHAPE        # a page's rows span >= 2 GiB
     assert indexer(rg(), cache(dtype=B.MSA_DTYPE_FP8_E4M3)) == DTYPE
     assert indexer(rg(), cache(dtype=7)) == DTYPE
     assert indexer(rg(), cache(), top_k=0) == PARAM
@@ -73,6 +74,7 @@ def test_attention_validation():
     assert attention(rg(), k, v, top_k=0) == PARAM
     assert attention(rg(), k, v, np_=65) == PARAM
     assert attention(rg(), k, v, scale=float("nan")) == PARAM
+    assert attention(rg(), cache(heads=8, tok=1 << 23), v) == SHAPE   # page span >= 2 GiB
     assert attention(rg(), k, v, scale=0.0) == PARAM
     assert attention(rg(), k, v, scale=-0.1) == PARAM
     assert attention(rg(), k, v, scale=float("inf")) == PARAM
