@@ -9,18 +9,15 @@
 //     that the host only sizes): for every (sequence, tile of tokens, KV
 //     head) the ascending union of the blocks the tile's tokens selected,
 //     the page of each, and a bit mask of which tokens selected it.
-//   * attn_prefill_kernel -- MFMA attention over each tile's union blocks;
-//     K and V tiles are staged in LDS once per workgroup and shared by its
-//     eight waves, each wave skipping blocks none of its tokens selected.
+//   * attn_prefill3_kernel -- MFMA attention over each tile's union blocks;
+//     K and V tiles are DMA'd into LDS once per workgroup and shared by its
+//     sixteen waves, each wave skipping blocks none of its tokens selected.
 //
 // The indexer's K tile in LDS is 128 rows of 256 bytes; 16-byte column c of
 // row pos is stored at column c ^ (pos & 15), so the 16 rows an MFMA
-// A-operand read touches fall in distinct bank groups.
-//
-// Both kernels double-buffer the tiles: the global loads of block e + 1 are
-// issued before block e is computed and written to LDS after it, with the
-// raw bits held in registers in between (any conversion happens at the LDS
-// store so that the loads stay in flight during the compute).
+// A-operand read touches fall in distinct bank groups.  Its loads are
+// double-buffered through registers: the global loads of block e + 1 are
+// issued before block e is computed and written to LDS after it.
 #include <algorithm>
 
 #include "msa_common.h"
@@ -352,45 +349,7 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
   if (lane == 0) p.plan_cnt[slot] = cnt;
 }
 
-// ---------------------------------------------------------------------------
-// Prefill attention: workgroup = 8 waves over one (sequence, tile of tq
-// tokens, KV head).  Wave w owns columns [w * cpw, (w + 1) * cpw) of the
-// tile's tq * G (token, query head) columns, as 16 * NCT MFMA columns.
-//
-// LDS rows are padded to 272 bytes (the 16 rows one MFMA operand read
-// touches then start in distinct bank groups), which keeps every operand
-// address a per-lane base plus a compile-time offset.
-// ---------------------------------------------------------------------------
-constexpr int kPrefillWaves = 8;
-constexpr int kRingHalf = 256;
-constexpr int kPitch = 272;                  // bytes per padded LDS row
-constexpr int kTileBytes = kBlock * kPitch;  // 34 KiB
-
-template <bool FP8>
-struct TileRegs;
-template <>
-struct TileRegs<false> {     // BF16: 4 K chunks and 4 V row slices of 16 B
-  u32x4 k[4];
-  u32x4 v[4];
-};
-template <>
-struct TileRegs<true> {      // FP8: 2 K chunks of 16 B and 4 V row slices of 8 B
-  u32x4 k[2];
-  u32x2 v[4];
-};
-
-// LDS of one prefill attention workgroup.  K tile: row = position.  V^T
-// tile: row = head dim d, with positions permuted inside each 32-position
-// chunk (32ch + 16a + 4g + i -> 32ch + 8g + 4a + i) so one 16-byte read
-// returns exactly the 8 positions of a lane's P^T B-operand.  Plan entries
-// pass through a ring of 2 * kRingHalf entries refilled half a ring at a
-// time, far ahead of use.
-struct PrefillLds {
-  char ks[2][kTileBytes];
-  char vt[2][kTileBytes];
-  int32_t ring_blk[2 * kRingHalf], ring_pg[2 * kRingHalf];
-  uint32_t ring_msk[2 * kRingHalf];
-};
+constexpr int kRingHalf = 256;   // plan entries per half of the LDS ring
 
 __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams p) {
   extern __shared__ int hist[];
@@ -398,295 +357,32 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams
   schedule_by_cost(nslots, p.nbmax, [&](int i) { return p.plan_cnt[i]; }, p.worklist, p.sched, hist);
 }
 
-template <bool FP8, int NCT>
-__device__ void attn_prefill_tile(const AttnParams& p, int slot, PrefillLds& L) {
-  auto& ks = L.ks;
-  auto& vt = L.vt;
-  auto& ring_blk = L.ring_blk;
-  auto& ring_pg = L.ring_pg;
-  auto& ring_msk = L.ring_msk;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int h = slot % p.H_kv;
-  const int tile = (slot / p.H_kv) % p.ntiles;
-  const int b = slot / p.H_kv / p.ntiles;
-  const int r0 = p.rg.offs[b];
-  const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
-  const int t0 = tile * p.tq;
-  if (t0 >= n) return;
-  const int c = p.rg.clen[b];
-  const int ntok = min(p.tq, n - t0);
-  const int p_tile_max = c + t0 + ntok - 1;
-  const int cnt = p.plan_cnt[slot];
-  const int32_t* ids = p.plan_ids + (size_t)slot * p.nbmax;
-  const int32_t* pgs = p.plan_pages + (size_t)slot * p.nbmax;
-  const uint32_t* msks = p.plan_mask + (size_t)slot * p.nbmax;
-
-  // ---- columns of this wave ---------------------------------------------
-  const int cpw = p.tq * p.G / kPrefillWaves;       // columns per wave (<= 16 * NCT)
-  const int tok_lo = wave * cpw / p.G;               // first token of the wave
-  const int tok_n = cpw / p.G;
-  uint32_t wave_bits = 0u;
-  for (int t = tok_lo; t < tok_lo + tok_n && t < ntok; ++t) wave_bits |= 1u << t;
-  int plim_col[NCT], tl_col[NCT];
-  u32x4 qf[NCT][4];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int cw = ct * 16 + l16;
-    const int cg = wave * cpw + cw;
-    tl_col[ct] = cg / p.G;
-    const bool ok = cw < cpw && tl_col[ct] < ntok;
-    plim_col[ct] = ok ? c + t0 + tl_col[ct] : -1;
-    const uint16_t* qp = p.q + ((size_t)(r0 + t0 + tl_col[ct]) * p.H_q + h * p.G + cg % p.G) * kDim;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[ct][s] = ok ? ld16(qp + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int p_wave_min = c + t0 + tok_lo;
-
-  f32x4 O[8][NCT];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NCT], l_run[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    m_run[ct] = neg_inf();
-    l_run[ct] = 0.f;
-  }
-  const float sc = p.scale_log2;
-  // operand read bases: K row 16pt + l16 at 16-byte column 4s + g, V^T row
-  // 16dt + l16 at column 4ch + g; (pt, s, dt, ch) only add constants
-  const int rd_base = l16 * kPitch + 16 * g;
-
-  // ---- staging: K rows and V transposed --------------------------------
-  const int esz = FP8 ? 1 : 2;
-  const char* kpool = static_cast<const char*>(p.k.data);
-  const char* vpool = static_cast<const char*>(p.v.data);
-  const size_t kts = (size_t)p.k.token_stride * esz, vts = (size_t)p.v.token_stride * esz;
-  const size_t khead = (size_t)h * p.k.head_stride * esz, vhead = (size_t)h * p.v.head_stride * esz;
-  const size_t kps = (size_t)p.k.page_stride * esz, vps = (size_t)p.v.page_stride * esz;
-  // V sub-block of this thread: rows 32ch + 16a + 4gq + i (i = 0..3), dims 8dg..8dg+7
-  const int v_dg = tid & 15, v_gq = (tid >> 4) & 3, v_a = (tid >> 6) & 1, v_ch = tid >> 7;
-  const int v_row0 = 32 * v_ch + 16 * v_a + 4 * v_gq;
-  const int vt_wr = (8 * v_dg) * kPitch + (4 * v_ch + v_gq) * 16 + 8 * v_a;
-  TileRegs<FP8> st;
-
-  auto stage_load = [&](int pg) {
-    if (pg < 0) pg = 0;
-    const char* kb = kpool + (size_t)pg * kps + khead;
-    const char* vb = vpool + (size_t)pg * vps + vhead;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int cidx = tid + 512 * k;     // 16 e4m3 values: position cidx >> 3, dims 16 * (cidx & 7)
-        st.k[k] = ld16(kb + (cidx >> 3) * kts + (cidx & 7) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.v[i] = ld8(vb + (v_row0 + i) * vts + 8 * v_dg);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int cidx = tid + 512 * k;     // 8 bf16 values: position cidx >> 4, dims 8 * (cidx & 15)
-        st.k[k] = ld16(kb + (cidx >> 4) * kts + (cidx & 15) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.v[i] = ld16(vb + (v_row0 + i) * vts + 16 * v_dg);
-    }
-  };
-  auto stage_store = [&](int buf, int blk) {
-    u32x4 vr[4];
-    if constexpr (FP8) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int cidx = tid + 512 * k;
-        char* dst = ks[buf] + (cidx >> 3) * kPitch + (cidx & 7) * 32;
-        *reinterpret_cast<u32x4*>(dst) = fp8x8_to_bf16x8(u32x2{st.k[k].x, st.k[k].y});
-        *reinterpret_cast<u32x4*>(dst + 16) = fp8x8_to_bf16x8(u32x2{st.k[k].z, st.k[k].w});
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vr[i] = fp8x8_to_bf16x8(st.v[i]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int cidx = tid + 512 * k;
-        *reinterpret_cast<u32x4*>(ks[buf] + (cidx >> 4) * kPitch + (cidx & 15) * 16) = st.k[k];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vr[i] = st.v[i];
-    }
-    // rows past every token of the tile hold no data: zero them so that a
-    // zero probability never meets a NaN
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (blk * kBlock + v_row0 + i > p_tile_max) vr[i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const u32x2 w = {pick_halves(vr[0][e >> 1], vr[1][e >> 1], e & 1),
-                       pick_halves(vr[2][e >> 1], vr[3][e >> 1], e & 1)};
-      *reinterpret_cast<u32x2*>(vt[buf] + vt_wr + e * kPitch) = w;
-    }
-  };
-
-  auto ring_fill = [&](int first) {   // entries first .. first + kRingHalf - 1
-    if (tid < kRingHalf) {
-      const int i = first + tid;
-      if (i < cnt) {
-        const int slot_i = i & (2 * kRingHalf - 1);
-        ring_blk[slot_i] = ids[i];
-        ring_pg[slot_i] = pgs[i];
-        ring_msk[slot_i] = msks[i];
-      }
-    }
-  };
-  ring_fill(0);
-  ring_fill(kRingHalf);
-  __syncthreads();
-  if (cnt > 0) {
-    stage_load(ring_pg[0]);
-    stage_store(0, ring_blk[0]);
-  }
-  for (int e = 0; e < cnt; ++e) {
-    const int buf = e & 1;
-    __syncthreads();
-    // entries e - kRingHalf .. e - 1 are consumed: reuse their slots
-    if (e >= kRingHalf && (e & (kRingHalf - 1)) == 0) ring_fill(e + kRingHalf);
-    const bool more = e + 1 < cnt;
-    const int rn = (e + 1) & (2 * kRingHalf - 1);
-    if (more) stage_load(ring_pg[rn]);
-    const int rc = e & (2 * kRingHalf - 1);
-    const int blk = uniform(ring_blk[rc]);
-    const uint32_t msk = uniform(ring_msk[rc]);
-    if (msk & wave_bits) {
-      // causal clip needed only where the block reaches past the wave's
-      // first token; elsewhere a column either reads the whole block or none
-      const bool diag = blk * kBlock + kBlock - 1 > p_wave_min;
-      bool live[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) live[ct] = plim_col[ct] >= 0 && ((msk >> tl_col[ct]) & 1u);
-      const char* kt = ks[buf] + rd_base;
-      const char* vtt = vt[buf] + rd_base;
-#pragma unroll 1
-      for (int hb = 0; hb < 2; ++hb) {
-        const char* kth = kt + 64 * hb * kPitch;
-        f32x4 S[4][NCT];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(kth + 16 * pt * kPitch + 64 * s);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-              S[pt][ct] = mfma_bf16(a, qf[ct][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[pt][ct]);
-          }
-        }
-        // online softmax per column, running max in scaled log2 units; a
-        // column that does not read this block keeps its state (its
-        // probabilities come out as exp2(-inf) = 0)
-        bool rescale = false;
-        float alpha[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          if (diag) {
-            const int lim = (live[ct] ? plim_col[ct] : -1) - (blk * kBlock + 64 * hb + 4 * g);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (16 * pt + i > lim) S[pt][ct][i] = neg_inf();
-          }
-          float hmax = neg_inf();
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt)
-            hmax = fmaxf(hmax, fmaxf(fmaxf(S[pt][ct][0], S[pt][ct][1]), fmaxf(S[pt][ct][2], S[pt][ct][3])));
-          hmax = colgroup_max(hmax) * sc;
-          const float m_new = live[ct] ? fmaxf(m_run[ct], hmax) : m_run[ct];
-          const float m_use = m_new == neg_inf() ? 0.f : m_new;
-          const float off = live[ct] ? m_use : __builtin_inff();
-          alpha[ct] = live[ct] ? fast_exp2(m_run[ct] - m_use) : 1.f;
-          rescale |= alpha[ct] != 1.f;
-          float lsum = 0.f;
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float e2 = fast_exp2(__builtin_fmaf(S[pt][ct][i], sc, -off));
-              S[pt][ct][i] = e2;
-              lsum += e2;
-            }
-          l_run[ct] = l_run[ct] * alpha[ct] + lsum;
-          m_run[ct] = m_new;
-        }
-        if (__builtin_amdgcn_ballot_w64(rescale)) {
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) O[dt][ct] *= alpha[ct];
-        }
-        // O^T += V^T P^T over the two 32-position chunks of this half
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          u32x4 bp[NCT];
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 s0 = S[2 * cc][ct], s1 = S[2 * cc + 1][ct];
-            bp[ct] = u32x4{pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]), pack_bf16(s1[0], s1[1]),
-                           pack_bf16(s1[2], s1[3])};
-          }
-          const char* vtc = vtt + 64 * (2 * hb + cc);
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(vtc + 16 * dt * kPitch);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = mfma_bf16(a, bp[ct], O[dt][ct]);
-          }
-        }
-      }
-    }
-    if (more) stage_store(buf ^ 1, uniform(ring_blk[rn]));
-  }
-
-  // ---- epilogue ------------------------------------------------------------
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const float l_tot = colgroup_sum(l_run[ct]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (plim_col[ct] < 0) continue;
-    const int cg = wave * cpw + ct * 16 + l16;
-    uint16_t* op = p.out + ((size_t)(r0 + t0 + tl_col[ct]) * p.H_q + h * p.G + cg % p.G) * kDim + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 o = O[dt][ct];
-      *reinterpret_cast<u32x2*>(op + 16 * dt) = u32x2{pack_bf16(o[0] * inv, o[1] * inv),
-                                                     pack_bf16(o[2] * inv, o[3] * inv)};
-    }
-  }
-}
-
-template <bool FP8, int NCT>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) PrefillLds lds;
-  __shared__ int item_s;
-  for (;;) {
-    const int k = take_item(p.sched, &item_s);
-    if (k < 0) break;
-    attn_prefill_tile<FP8, NCT>(p, p.worklist[k], lds);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// BF16 prefill attention with direct global->LDS tile loads.
+// Prefill attention with direct global->LDS tile loads, BF16 or FP8 KV.
 //
-// Workgroup = 8 waves (two per SIMD) of 16 * NCT columns each.  K and V tiles are DMA'd
-// straight into LDS, row-major, 256-byte rows with 16-byte column c of row
-// pos stored at column c ^ (pos & 15); each lane of a DMA instruction picks
-// its source so that its fixed LDS slot receives the right swizzled piece.
-// The PV A-operand (V^T) comes from two ds_read_b64_tr_b16 per fragment:
-// within each 16-lane group, output lane i, element k is element i % 4 of
-// source lane i / 4 + 4k, so source lane j reads row 16r + 4g + j / 4 at
-// dims 16dt + 4(j % 4), which yields for lane (m, g) the positions
-// 16r + 4g + k of dim 16dt + m -- exactly the P^T B-operand layout.
+// Workgroup = 16 waves (four per SIMD), persistent over the slot work list;
+// wave w owns columns [w cpw, (w + 1) cpw) of the tile's tq * G (token,
+// query head) columns, as 16 * NCT MFMA columns.  K and V tiles are DMA'd
+// straight into LDS, row-major (256-byte rows for BF16, 128-byte rows for
+// FP8), with an XOR swizzle of 16-byte columns; each lane of a DMA
+// instruction picks its source so that its fixed LDS slot receives the right
+// swizzled piece.
+//
+// BF16: column c of row pos is stored at c ^ (pos & 15).  The PV A-operand
+// (V^T) comes from two ds_read_b64_tr_b16 per fragment: within each 16-lane
+// group, output lane i, element k is element i % 4 of source lane i / 4 +
+// 4k, so source lane j reads row 16r + 4g + j / 4 at dims 16dt + 4(j % 4),
+// which yields for lane (m, g) the positions 16r + 4g + k of dim 16dt + m --
+// exactly the P^T B-operand layout.
+//
+// FP8 (e4m3, widened to BF16 in registers as operands are read): K column c
+// of row pos sits at c ^ ((pos >> 1) & 7), V column c at c ^ fv(pos) built
+// from bits 1, 4 and 2 of pos; that keeps the 16 rows of a K operand read
+// and the 8 rows of a transposed V read in distinct bank groups.  V^T comes
+// from one ds_read_b64_tr_b8 per fragment: within each 16-lane group, output
+// lane i, element k is byte i % 8 of source lane i / 8 + 2k, so source lanes
+// 2k and 2k + 1 read the row holding P^T position k at dims 16dt and
+// 16dt + 8, and lane (m, g) receives the 8 positions of dim 16dt + m.
 // ---------------------------------------------------------------------------
 constexpr int kP3Waves = 16;
 constexpr float kLazy = 8.f;   // log2 headroom before the running max moves
@@ -699,11 +395,18 @@ struct PrefillLds3 {
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ __forceinline__ u32x2 lds_tr8(const char* p) {
+// 8-byte transposing LDS reads of 16-bit and of 8-bit elements
+__device__ __forceinline__ u32x2 lds_tr_b16(const char* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x2 lds_tr_b8(const char* p) {
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_char*)p);
   return __builtin_bit_cast(u32x2, v);
 }
 
@@ -711,8 +414,16 @@ __device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_char*)lds_dst, 16, 0, 0);
 }
 
-template <int NCT>
+// FP8 tile swizzles (16-byte column XOR masks of row pos)
+__device__ __forceinline__ int fp8_kswz(int pos) { return (pos >> 1) & 7; }
+__device__ __forceinline__ int fp8_vswz(int pos) {
+  return ((pos >> 1) & 1) | (((pos >> 4) & 1) << 1) | (((pos >> 2) & 1) << 2);
+}
+
+template <bool FP8, int NCT>
 __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L) {
+  constexpr int RB = FP8 ? 128 : 256;       // bytes per LDS tile row
+  constexpr int ESZ = FP8 ? 1 : 2;          // bytes per cache element
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -766,32 +477,51 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   const float sc = p.scale_log2;
 
   // ---- lane-constant LDS addresses ---------------------------------------
-  // K A-operand: row 16pt + l16 (+ 64hb), logical column 4s + g
+  // BF16 K A-operand: row 16pt + l16 (+ 64hb), logical column 4s + g
   //   = l16 * 256 + ((4s + g) ^ l16) * 16 = kq ^ (s << 6), kq for s = 0
-  const int kq = l16 * 256 + ((g ^ l16) << 4);
-  // V^T A-operand (transpose read r of chunk ch, dim tile dt): row
-  // 32ch + 16r + q with q = 4g + l16 / 4, dims 16dt + 4(l16 % 4)
+  // FP8 K A-operand: row 16pt + l16 (+ 64hb), bytes 32s + 8g.. = logical
+  //   column 2s + g / 2, half g % 2: with x = (g / 2) ^ kswz(l16),
+  //   l16 * 128 + ((2s ^ x) << 4) + 8 (g % 2) = kq ^ (s << 5)
+  const int kq = FP8 ? l16 * 128 + ((((g >> 1) ^ fp8_kswz(l16))) << 4) + 8 * (g & 1)
+                     : l16 * 256 + ((g ^ l16) << 4);
+  // BF16 V^T A-operand (transpose read r of chunk ch, dim tile dt): row
+  //   32ch + 16r + q with q = 4g + l16 / 4, dims 16dt + 4(l16 % 4)
   //   = (32ch + 16r) * 256 + (vq ^ (dt << 5))
-  const int vq_row = 4 * g + (l16 >> 2);
-  const int vq = vq_row * 256 + (((((l16 & 3) >> 1)) ^ vq_row) << 4) + 8 * (l16 & 1);
-  // DMA: instruction i of this wave covers rows 16 wave + 4i .. + 3; lane
-  // lands in row 16 wave + 4i + lane / 16 at physical column lane % 16
-  const int dr = lane >> 4, dc = lane & 15;
+  // FP8 V^T A-operand (one transpose read of chunk ch, dim tile dt): source
+  //   lane l16 reads P^T position k = l16 / 2, i.e. row
+  //   32ch + 16(k / 4) + 4g + k % 4, at dims 16dt + 8 (l16 % 2)
+  //   = 32ch * 128 + (vq ^ (dt << 4))
+  int vq;
+  if constexpr (FP8) {
+    const int k = l16 >> 1;
+    const int vrow = 16 * (k >> 2) + 4 * g + (k & 3);
+    vq = vrow * 128 + (fp8_vswz(vrow) << 4) + 8 * (l16 & 1);
+  } else {
+    const int vq_row = 4 * g + (l16 >> 2);
+    vq = vq_row * 256 + (((((l16 & 3) >> 1)) ^ vq_row) << 4) + 8 * (l16 & 1);
+  }
+  // DMA: instruction i of this wave covers kRowsPerDma rows from
+  // kRowsPerWave * wave + kRowsPerDma * i; a lane lands in row
+  // + lane / (RB / 16) at physical column lane % (RB / 16)
+  constexpr int kCols = RB / 16;                      // 16-byte columns per row
+  constexpr int kRowsPerDma = 64 / kCols;
+  constexpr int kRowsPerWave = kBlock / kP3Waves;     // tile rows each wave fetches
+  constexpr int kDmaPerWave = kRowsPerWave / kRowsPerDma;
+  const int dr = lane / kCols, dc = lane % kCols;
   const char* kpool = static_cast<const char*>(p.k.data);
   const char* vpool = static_cast<const char*>(p.v.data);
-  const uint32_t kts = (uint32_t)p.k.token_stride * 2, vts = (uint32_t)p.v.token_stride * 2;
-  const size_t khead = (size_t)h * p.k.head_stride * 2, vhead = (size_t)h * p.v.head_stride * 2;
-  const size_t kps = (size_t)p.k.page_stride * 2, vps = (size_t)p.v.page_stride * 2;
+  const uint32_t kts = (uint32_t)p.k.token_stride * ESZ, vts = (uint32_t)p.v.token_stride * ESZ;
+  const size_t khead = (size_t)h * p.k.head_stride * ESZ, vhead = (size_t)h * p.v.head_stride * ESZ;
+  const size_t kps = (size_t)p.k.page_stride * ESZ, vps = (size_t)p.v.page_stride * ESZ;
   // byte offsets (within a tile) of the pieces this lane fetches
-  constexpr int kRowsPerWave = kBlock / kP3Waves;      // tile rows each wave fetches
-  constexpr int kDmaPerWave = kRowsPerWave / 4;         // 4 rows per DMA instruction
   uint32_t koff[kDmaPerWave], voff[kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
-    const int row = kRowsPerWave * wave + 4 * i + dr;
-    const uint32_t col = (dc ^ (row & 15)) << 4;
-    koff[i] = row * kts + col;
-    voff[i] = row * vts + col;
+    const int row = kRowsPerWave * wave + kRowsPerDma * i + dr;
+    const uint32_t kcol = (FP8 ? dc ^ fp8_kswz(row) : dc ^ (row & 15)) << 4;
+    const uint32_t vcol = (FP8 ? dc ^ fp8_vswz(row) : dc ^ (row & 15)) << 4;
+    koff[i] = row * kts + kcol;
+    voff[i] = row * vts + vcol;
   }
 
   auto stage = [&](int pg, int buf) {
@@ -800,8 +530,8 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     const char* vb = vpool + (size_t)pg * vps + vhead;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      dma16(kb + koff[i], L.k[buf] + (kRowsPerWave * wave + 4 * i) * 256);
-      dma16(vb + voff[i], L.v[buf] + (kRowsPerWave * wave + 4 * i) * 256);
+      dma16(kb + koff[i], L.k[buf] + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
+      dma16(vb + voff[i], L.v[buf] + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
     }
   };
 
@@ -833,10 +563,10 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     // tile's last block can have such rows) so that a zero probability never
     // meets a NaN
     if (blk * kBlock + kBlock - 1 > p_tile_max) {
-      for (int i = tid; i < kBlock * 16; i += kP3Waves * 64) {
-        const int row = i >> 4;
+      for (int i = tid; i < kBlock * kCols; i += kP3Waves * 64) {
+        const int row = i / kCols;
         if (blk * kBlock + row > p_tile_max)
-          *reinterpret_cast<u32x4*>(L.v[buf] + row * 256 + (i & 15) * 16) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(L.v[buf] + row * RB + (i % kCols) * 16) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
     }
@@ -860,7 +590,11 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + (64 * hb + 16 * pt) * 256 + (kq ^ (s << 6)));
+          u32x4 a;
+          if constexpr (FP8)
+            a = fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>(kt + (64 * hb + 16 * pt) * RB + (kq ^ (s << 5))));
+          else
+            a = *reinterpret_cast<const u32x4*>(kt + (64 * hb + 16 * pt) * RB + (kq ^ (s << 6)));
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct)
             Sh[pt][ct] = mfma_bf16(a, qf[ct][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : Sh[pt][ct]);
@@ -932,10 +666,15 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
         const int chunk = 2 * hb + cc;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const char* base = vtl + (32 * chunk) * 256 + (vq ^ (dt << 5));
-          const u32x2 lo = lds_tr8(base);
-          const u32x2 hi = lds_tr8(base + 16 * 256);
-          const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+          u32x4 a;
+          if constexpr (FP8) {
+            a = fp8x8_to_bf16x8(lds_tr_b8(vtl + (32 * chunk) * RB + (vq ^ (dt << 4))));
+          } else {
+            const char* base = vtl + (32 * chunk) * RB + (vq ^ (dt << 5));
+            const u32x2 lo = lds_tr_b16(base);
+            const u32x2 hi = lds_tr_b16(base + 16 * RB);
+            a = u32x4{lo.x, lo.y, hi.x, hi.y};
+          }
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = mfma_bf16(a, bp[ct], O[dt][ct]);
         }
@@ -961,26 +700,22 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   }
 }
 
-template <int NCT>
+template <bool FP8, int NCT>
 __global__ __launch_bounds__(64 * kP3Waves) void attn_prefill3_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) PrefillLds3 lds;
   __shared__ int item_s;
   for (;;) {
     const int k = take_item(p.sched, &item_s);
     if (k < 0) break;
-    attn_prefill3_tile<NCT>(p, p.worklist[k], lds);
+    attn_prefill3_tile<FP8, NCT>(p, p.worklist[k], lds);
   }
 }
 
-void prefill_tiling(int G, bool fp8, int* tq, int* nct) {
-  if (fp8) {   // staged kernel: 8 waves, 16 * nct columns each
-    *tq = G >= 16 ? 16 : 32;
-    *nct = *tq * G / kPrefillWaves > 16 ? 2 : 1;
-  } else {     // direct-load kernel: kP3Waves waves of at most 32 columns
-    *tq = std::min(32, kP3Waves * 32 / G);
-    const int cpw = *tq * G / kP3Waves;
-    *nct = cpw > 16 ? 2 : 1;
-  }
+void prefill_tiling(int G, bool /*fp8*/, int* tq, int* nct) {
+  // kP3Waves waves of at most 32 columns, both KV types
+  *tq = std::min(32, kP3Waves * 32 / G);
+  const int cpw = *tq * G / kP3Waves;
+  *nct = cpw > 16 ? 2 : 1;
 }
 
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s) {
@@ -994,15 +729,13 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s
   if (e != hipSuccess) return e;
   int tq, nct;
   prefill_tiling(p.G, fp8, &tq, &nct);
-  const dim3 grid((unsigned)p.nwg);
+  const dim3 grid((unsigned)p.nwg), block(64 * kP3Waves);
   if (fp8) {
-    const dim3 block(64 * kPrefillWaves);
-    if (nct == 2) hipLaunchKernelGGL((attn_prefill_kernel<true, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill_kernel<true, 1>), grid, block, 0, s, p);
+    if (nct == 2) hipLaunchKernelGGL((attn_prefill3_kernel<true, 2>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<true, 1>), grid, block, 0, s, p);
   } else {
-    const dim3 block(64 * kP3Waves);
-    if (nct == 2) hipLaunchKernelGGL((attn_prefill3_kernel<2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill3_kernel<1>), grid, block, 0, s, p);
+    if (nct == 2) hipLaunchKernelGGL((attn_prefill3_kernel<false, 2>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
