@@ -387,9 +387,12 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams
 constexpr int kP3Waves = 16;
 constexpr float kLazy = 8.f;   // log2 headroom before the running max moves
 
+// Tile ring: 64 KiB each for K and V, i.e. two BF16 stages or four FP8
+// stages of one 128-position block.
+constexpr int kRingBytes = 2 * kBlock * 256;
 struct PrefillLds3 {
-  char k[2][kBlock * 256];
-  char v[2][kBlock * 256];
+  char k[kRingBytes];
+  char v[kRingBytes];
   int32_t ring_blk[2 * kRingHalf], ring_pg[2 * kRingHalf];
   uint32_t ring_msk[2 * kRingHalf];
 };
@@ -410,9 +413,27 @@ __device__ __forceinline__ u32x2 lds_tr_b8(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Global -> LDS copy of 16 bytes per lane: lane L's bytes land at lds_dst +
+// 16 L (lds_dst is wave-uniform).  Written as inline asm (M0 = LDS address,
+// one wait state, the DMA; no register outputs) rather than the builtin,
+// because the compiler treats a builtin DMA as a pending LDS write and waits
+// for every one of them before any later LDS read, which would drain the
+// tile ring on every block.  The callers order each stage's reads after its
+// DMA themselves: an explicit vmcnt wait for this wave's own DMA, then a
+// workgroup barrier for everyone else's.
+// M0 is reserved to the compiler, which warns about the clobber; nothing in
+// these kernels keeps a value in M0 across a DMA (every M0 write in the
+// generated code is the one above its DMA).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_char*)lds_dst, 16, 0, 0);
+  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)(lds_char*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // FP8 tile swizzles (16-byte column XOR masks of row pos)
 __device__ __forceinline__ int fp8_kswz(int pos) { return (pos >> 1) & 7; }
@@ -424,6 +445,8 @@ template <bool FP8, int NCT>
 __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L) {
   constexpr int RB = FP8 ? 128 : 256;       // bytes per LDS tile row
   constexpr int ESZ = FP8 ? 1 : 2;          // bytes per cache element
+  constexpr int TILE = kBlock * RB;         // bytes of one K (or V) tile
+  constexpr int NST = kRingBytes / TILE;    // ring stages: 2 (BF16), 4 (FP8)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -530,8 +553,8 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     const char* vb = vpool + (size_t)pg * vps + vhead;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      dma16(kb + koff[i], L.k[buf] + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
-      dma16(vb + voff[i], L.v[buf] + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
+      dma16(kb + koff[i], L.k + buf * TILE + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
+      dma16(vb + voff[i], L.v + buf * TILE + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
     }
   };
 
@@ -549,12 +572,28 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   ring_fill(0);
   ring_fill(kRingHalf);
   __syncthreads();
-  if (cnt > 0) stage(L.ring_pg[0], 0);
+  // the first NST - 1 blocks are requested up front; block e + NST - 1 is
+  // requested once block e's barrier shows that every wave is done with the
+  // stage it reuses
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j)
+    if (j < cnt) stage(L.ring_pg[j], j);
 
   for (int e = 0; e < cnt; ++e) {
-    const int buf = e & 1;
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's DMA into buf has landed
-    __syncthreads();                   // ... and every other wave's
+    const int buf = e % NST;
+    // this wave's DMA into buf has landed: at most the DMA instructions of
+    // the NST - 2 younger blocks may still be in flight (vmcnt counts this
+    // wave's vector-memory operations in issue order; lgkm and exp untouched)
+    constexpr int kYounger = 2 * kDmaPerWave * (NST - 2);
+    static_assert(kYounger < 16, "vmcnt immediate holds 4 bits here");
+    if (NST > 2 && e + NST - 2 < cnt) __builtin_amdgcn_s_waitcnt(0xF70 | kYounger);
+    else __builtin_amdgcn_s_waitcnt(0xF70);
+    // ... and every other wave's.  A bare barrier: a fenced one would also
+    // wait for the younger DMAs still in flight.  Nothing before it needs
+    // ordering: LDS traffic of block e - 1 was consumed by this wave's MFMAs,
+    // and the ring and zeroing writes have barriers of their own.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
     if (e >= kRingHalf && (e & (kRingHalf - 1)) == 0) ring_fill(e + kRingHalf);
     const int rc = e & (2 * kRingHalf - 1);
     const int blk = uniform(L.ring_blk[rc]);
@@ -566,19 +605,19 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
       for (int i = tid; i < kBlock * kCols; i += kP3Waves * 64) {
         const int row = i / kCols;
         if (blk * kBlock + row > p_tile_max)
-          *reinterpret_cast<u32x4*>(L.v[buf] + row * RB + (i % kCols) * 16) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(L.v + buf * TILE + row * RB + (i % kCols) * 16) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
     }
-    if (e + 1 < cnt) stage(L.ring_pg[(e + 1) & (2 * kRingHalf - 1)], buf ^ 1);
+    if (e + NST - 1 < cnt) stage(L.ring_pg[(e + NST - 1) & (2 * kRingHalf - 1)], (e + NST - 1) % NST);
     if (!(msk & wave_bits)) continue;
 
     const bool diag = blk * kBlock + kBlock - 1 > p_wave_min;
     bool live[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) live[ct] = plim_col[ct] >= 0 && ((msk >> tl_col[ct]) & 1u);
-    const char* kt = L.k[buf];
-    const char* vtl = L.v[buf];
+    const char* kt = L.k + buf * TILE;
+    const char* vtl = L.v + buf * TILE;
 
     // S^T for the block: with few columns both halves are computed up front
     // so that the second half's MFMAs can overlap the first half's softmax;
