@@ -22,6 +22,9 @@ MSA_DTYPE_BF16 = 0
 MSA_DTYPE_FP8_E4M3 = 1
 BLOCK = 128
 HEAD_DIM = 128
+MSA_MAX_SPEC_DRAFT = 8    # largest new-token count routed as speculative decode
+MSA_MAX_BLOCKS = 8192     # most blocks one sequence may hold
+MSA_MAX_TOPK = 512        # largest top_k
 
 
 class MsaError(RuntimeError):

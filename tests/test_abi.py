@@ -2,6 +2,7 @@
 host-side validation rejects bad arguments before touching any device.
 CPU only: none of these calls reaches a kernel launch or a device query."""
 import ctypes
+import re
 
 import pytest
 
@@ -17,6 +18,15 @@ def test_library_exports_every_declared_function():
     assert {"msa_indexer_paged", "msa_attention_paged", "msa_splitk_combine"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_binding_constants_match_header():
+    text = open(B.HEADER).read()
+    for name in ("MSA_MAX_SPEC_DRAFT", "MSA_MAX_BLOCKS", "MSA_MAX_TOPK", "MSA_DTYPE_BF16",
+                 "MSA_DTYPE_FP8_E4M3"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m, name
+        assert int(m.group(1)) == getattr(B, name), name
 
 
 def rg(batch=2, max_seq=1, max_cache=4000, stride=40, null=False):

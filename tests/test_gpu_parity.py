@@ -133,6 +133,22 @@ def test_many_sequences_per_scorer_chunk():
     run_and_check(wl, seqs=[0, 1, 2, 255, 256, 257, 298, 299])
 
 
+def test_maximum_context_and_top_k():
+    # MSA_MAX_BLOCKS blocks (1 Mi positions) and MSA_MAX_TOPK blocks per row:
+    # the widest top-k (8188 candidates) and the largest attention unions
+    full = B.MSA_MAX_BLOCKS * 128
+    run_and_check(wl_custom("max_decode", [1, 1], [full - 1, 3000 * 128 + 5], H_kv=2, G=2,
+                            top_k=B.MSA_MAX_TOPK, init=1, local=4))
+    run_and_check(wl_custom("max_prefill", [16], [full - 16], H_kv=1, G=4,
+                            top_k=B.MSA_MAX_TOPK, init=1, local=4), per_seq=6)
+
+
+def test_top_k_over_a_few_thousand_candidates():
+    # 1025..4096 candidates: the 64-keys-per-lane top-k
+    run_and_check(wl_custom("kpl64", [1, 3, 1], [3500 * 128, 2100 * 128 + 77, 1400 * 128], H_kv=2,
+                            top_k=100, init=2, local=3))
+
+
 def test_two_column_groups_per_sequence():
     # 16 KV heads sharing one index head x 8 draft tokens = 128 columns
     run_and_check(wl_custom("cg2", [8, 3, 6], [3000, 5000, 700], H_kv=16, G=1, top_k=5))
