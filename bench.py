@@ -14,11 +14,16 @@ the gathered-KV bytes the step must move divided by the step time (GB/s),
 with query tokens per second beside it; the prefill workload reports
 attention TFLOP/s instead.
 
+Timing: W untimed warmup steps, then exactly K steps bracketed by a device
+synchronize and two HIP events on the launch stream, with nothing else
+enqueued between them; value and ms_per_step come from the host wall clock
+over those K steps.
+
 Roofline: the dominant kernel is the sparse-attention kernel.  Its average
-duration is measured live with HIP events on the launch stream over the
-timed region (the attention call minus a separately timed combine of the
-same shape, since the call enqueues both); achieved = algorithmic bytes (or
-flops) of one launch / that duration.
+duration is measured live with HIP events on the launch stream: K
+back-to-back attention calls between two events, minus K back-to-back split-K
+combines of the same shape when the call enqueues one; achieved =
+algorithmic bytes (or flops) of one launch / that duration.
 
 CPU baseline: the oracle (plain NumPy, as written -- not tuned) timed on the
 host cores on a bounded sample of the same workload's rows.
@@ -208,11 +213,14 @@ def write_traffic_record(args):
         per = _counter_per_dispatch(path, counter)
         copy = max(v for name, vals in per.items() if "copy" in name.lower() for v in vals)
         attn = [v for name, vals in per.items() if "attn_decode_kernel" in name for v in vals]
+        comb = [v for name, vals in per.items() if "combine_kernel" in name for v in vals]
         if not attn:
             raise SystemExit(f"no attn_decode_kernel dispatch in {path}")
         scale = COPY_BYTES / (copy * 1024.0)
-        raw[counter] = (float(np.mean(attn)), copy, scale, len(attn))
-        scaled[counter] = float(np.mean(attn)) * 1024.0 * scale
+        # one attention call: the attention kernel, plus the combine when split
+        per_call = float(np.mean(attn)) + (float(np.mean(comb)) if comb else 0.0)
+        raw[counter] = (per_call, copy, scale, len(attn), float(np.mean(comb)) if comb else 0.0)
+        scaled[counter] = per_call * 1024.0 * scale
 
     wl = I.WORKLOADS[args.workload]()
     inp = I.make_inputs(wl, "cuda")
@@ -220,14 +228,17 @@ def write_traffic_record(args):
     torch.cuda.synchronize()
     algo = algorithmic_work(wl, d.cpu().numpy())["kv_bytes"]
     hbm = scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"]
-    cmd = ("rocprofv3 --pmc {c} --kernel-include-regex 'attn_decode_kernel|copy|elementwise' "
+    cmd = ("rocprofv3 --pmc {c} --kernel-include-regex "
+           "'attn_decode_kernel|combine_kernel|copy|elementwise' "
            "--output-format csv -d $R/gpurun_out/pmc_{w}_{l} -o run -- python3 $R/bench.py "
            "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration")
     rec = {
-        "kernel": "msa::attn_decode_kernel",
+        "kernel": ("msa::attn_decode_kernel" if not raw["FETCH_SIZE"][4] else
+                   "one attention call: msa::attn_decode_kernel + msa::combine_kernel"),
         "workload": f"{args.workload} ({wl.name})",
         "fetch_size_kib_per_launch": raw["FETCH_SIZE"][0],
         "write_size_kib_per_launch": raw["WRITE_SIZE"][0],
+        "combine_fetch_write_kib_per_launch": [raw["FETCH_SIZE"][4], raw["WRITE_SIZE"][4]],
         "dispatches_averaged": raw["FETCH_SIZE"][3],
         "calibration": {
             "fetch_scale": raw["FETCH_SIZE"][2], "write_scale": raw["WRITE_SIZE"][2],
@@ -290,18 +301,36 @@ def run(workload, args):
         attention()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+
+    # The timed region: K whole steps, nothing else on the stream.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(K):
-        ev[k][0].record(stream)
+    t_start.record(stream)
+    for _ in range(K):
         indexer()
-        ev[k][1].record(stream)
         attention()
-        ev[k][2].record(stream)
+    t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    gpu_step_ms = t_start.elapsed_time(t_end) / K
+
+    # Per-call averages on the launch stream: K back-to-back calls of one
+    # entry point between two HIP events (an event between the calls of a
+    # step would itself add a gap to the step).
+    def per_call_ms(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
+    att_ms = per_call_ms(attention)
+    idx_ms = per_call_ms(indexer)
 
     # The attention call also enqueues the combine when np > 1: time a combine
     # of the same shape on its own and subtract it.
@@ -310,14 +339,10 @@ def run(workload, args):
         rcap = wl.batch * wl.max_seq_length
         po = torch.zeros((np_, rcap, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
         pl = torch.zeros((np_, rcap, wl.num_q_heads), dtype=torch.float32, device="cuda")
-        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        for k in range(K):
-            ce[k][0].record(stream)
-            B.msa_splitk_combine(out, po, pl, inp.input_row_offsets, wl.batch, wl.max_seq_length,
-                                 np_, wl.num_q_heads, stream)
-            ce[k][1].record(stream)
         torch.cuda.synchronize()
-        comb_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ce]))
+        comb_ms = per_call_ms(lambda: B.msa_splitk_combine(out, po, pl, inp.input_row_offsets,
+                                                            wl.batch, wl.max_seq_length, np_,
+                                                            wl.num_q_heads, stream))
         attention()                       # restore the real output
         torch.cuda.synchronize()
     attn_kernel_ms = max(att_ms - comb_ms, 1e-6)
@@ -325,18 +350,27 @@ def run(workload, args):
     work = algorithmic_work(wl, d.cpu().numpy())
     ms = wall / K * 1e3
     tok_s = wl.total_rows / (wall / K)
+    # The roofline's duration is one attention call: the attention kernel
+    # alone on the decode routes with one partition; with split-K it also
+    # holds the combine launch (subtracting a separately timed combine would
+    # make the figure depend on launch gaps); on the prefill route it also
+    # holds the plan and schedule launches.
     if prefill:
         metric_value = work["attn_flops"] / (wall / K) / 1e12
         unit = "TFLOP/s"
-        achieved = work["attn_flops"] / (attn_kernel_ms * 1e-3) / 1e12
+        achieved = work["attn_flops"] / (att_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                "kernel": "prefill attention call: prefill_plan_kernel + attn_schedule_kernel + "
+                          "attn_prefill3_kernel"}
     else:
         metric_value = work["kv_bytes"] / (wall / K) / 1e9
         unit = "GB/s"
-        achieved = work["kv_bytes"] / (attn_kernel_ms * 1e-3) / 1e9
+        achieved = work["kv_bytes"] / (att_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload)}
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload),
+                "kernel": "attn_decode_kernel" if np_ == 1 else
+                          "attention call: attn_decode_kernel + combine_kernel (split-K)"}
     res = {
         "metric": "decode gathered-KV GB/s (% HBM peak) + query tok/s; prefill TFLOP/s (% MFMA)",
         "value": metric_value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -350,6 +384,7 @@ def run(workload, args):
                    "index_k_heads": wl.num_ik_heads, "split_k_partitions": np_},
         "query_tok_s": tok_s,
         "hbm_frac_of_step": (work["kv_bytes"] + work["ik_bytes"]) / (wall / K) / 1e9 / HBM_PEAK_GBPS,
+        "gpu_ms_per_step": gpu_step_ms,
         "kernels_ms": {"indexer_call": idx_ms, "attention_call": att_ms, "combine": comb_ms,
                        "attention_kernel": attn_kernel_ms},
         "algorithmic": work,
