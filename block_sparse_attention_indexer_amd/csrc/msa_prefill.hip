@@ -15,9 +15,9 @@
 //
 // The indexer's K tile in LDS is 128 rows of 256 bytes; 16-byte column c of
 // row pos is stored at column c ^ (pos & 15), so the 16 rows an MFMA
-// A-operand read touches fall in distinct bank groups.  Its loads are
-// double-buffered through registers: the global loads of block e + 1 are
-// issued before block e is computed and written to LDS after it.
+// A-operand read touches fall in distinct bank groups.  Both the indexer and
+// the attention kernel fetch tiles by global->LDS DMA into a ring of stages,
+// several blocks ahead of the one being computed.
 #include <algorithm>
 
 #include "msa_common.h"
@@ -30,6 +30,34 @@ __device__ __forceinline__ int k_off(int pos, int c16) { return pos * 256 + ((c1
 __device__ __forceinline__ u32x4 lds16(const char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Global -> LDS copy of 16 bytes per lane: lane L's bytes land at lds_dst +
+// 16 L (lds_dst is wave-uniform).  Written as inline asm (M0 = LDS address,
+// one wait state, the DMA; no register outputs) rather than the builtin,
+// because the compiler treats a builtin DMA as a pending LDS write and waits
+// for every one of them before any later LDS read, which would drain the
+// tile ring on every block.  The callers order each stage's reads after its
+// DMA themselves: an explicit vmcnt wait for this wave's own DMA, then a
+// workgroup barrier for everyone else's.
+// M0 is reserved to the compiler, which warns about the clobber; nothing in
+// these kernels keeps a value in M0 across a DMA (every M0 write in the
+// generated code is the one above its DMA).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
+  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)(lds_char*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits until at most n of this wave's vector-memory
+// operations are outstanding (lgkm and exp counters not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // ---------------------------------------------------------------------------
 // Work lists.  The prefill grids would otherwise be over-launched from host
@@ -149,13 +177,17 @@ __global__ __launch_bounds__(kSchedThreads) void indexer_schedule_kernel(Indexer
                    p.worklist, p.sched, hist);
 }
 
-__device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, char (*lds)[kBlock * 256],
+constexpr int kIdxTileBytes = kBlock * 256;   // one BF16 index-K tile
+
+template <int NST>
+__device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, char* ring,
                                      int32_t* pages_lds) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform((int)(tid >> 6));
   const int l16 = lane & 15, g = lane >> 4;
   const int hpi = p.H_kv / p.H_ik;
   const int blk_lo = T.blk_lo, blk_hi = T.blk_hi;
+  const int nblk = blk_hi - blk_lo;
 
   u32x4 qf[4][4];
   int plim[4], orow[4];
@@ -174,33 +206,36 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
   const int p_first = T.c + T.t0;
 
   const char* pool = static_cast<const char*>(p.ik.data);
-  const size_t ts = (size_t)p.ik.token_stride * 2;
-  const size_t head_off = (size_t)T.hk * p.ik.head_stride;
+  const uint32_t ts = (uint32_t)p.ik.token_stride * 2;
+  const size_t head_bytes = (size_t)T.hk * p.ik.head_stride * 2;
+  const size_t page_bytes = (size_t)p.ik.page_stride * 2;
   const int32_t* trow = p.rg.table + (size_t)T.b * p.rg.stride;
   const int npages = p.ik.num_pages;
   // The page ids of the whole block range go to LDS first, so the loop
   // never waits on a global load to learn where its next tile is.
-  for (int i = tid; i < blk_hi - blk_lo; i += 256) pages_lds[i] = trow[blk_lo + i];
+  for (int i = tid; i < nblk; i += 256) pages_lds[i] = trow[blk_lo + i];
   __syncthreads();
 
-  u32x4 stage[8];
-  auto tile_base = [&](int pg) -> const char* {
-    if ((unsigned)pg >= (unsigned)npages) pg = 0;
-    return pool + ((size_t)pg * p.ik.page_stride + head_off) * 2;
-  };
-  {
-    const char* kb = tile_base(pages_lds[0]);
+  // DMA: instruction i of this wave fills tile rows 32 wave + 4i .. + 3; a
+  // lane lands in row + lane / 16 at physical column lane % 16 and fetches
+  // the logical column that the swizzle puts there.
+  uint32_t doff[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int cidx = tid + 256 * k;
-      stage[k] = ld16(kb + (cidx >> 4) * ts + (cidx & 15) * 16);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int cidx = tid + 256 * k;
-      *reinterpret_cast<u32x4*>(lds[0] + k_off(cidx >> 4, cidx & 15)) = stage[k];
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int row = 32 * wave + 4 * i + (lane >> 4);
+    doff[i] = row * ts + ((((lane & 15) ^ (row & 15))) << 4);
   }
+  auto stage = [&](int rel, int buf) {
+    int pg = pages_lds[rel];
+    if ((unsigned)pg >= (unsigned)npages) pg = 0;
+    const char* kb = pool + (size_t)pg * page_bytes + head_bytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(kb + doff[i], ring + buf * kIdxTileBytes + (32 * wave + 4 * i) * 256);
+  };
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j)
+    if (j < nblk) stage(j, j);
+
   float win[4][4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
@@ -208,18 +243,16 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
     for (int j = 0; j < 4; ++j) win[ct][j] = 0.f;
 
   for (int blk = blk_lo; blk < blk_hi; ++blk) {
-    const int buf = (blk - blk_lo) & 1;
-    __syncthreads();
-    const bool more = blk + 1 < blk_hi;
-    if (more) {
-      const char* kb = tile_base(pages_lds[blk + 1 - blk_lo]);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int cidx = tid + 256 * k;
-        stage[k] = ld16(kb + (cidx >> 4) * ts + (cidx & 15) * 16);
-      }
-    }
-    const char* kt = lds[buf];
+    const int e = blk - blk_lo;
+    const int buf = e % NST;
+    // this wave's DMA of block e has landed (the 8 DMA instructions of each
+    // younger block may still be in flight), then everyone's has
+    if (NST > 2 && e + NST - 2 < nblk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * (NST - 2)));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (e + NST - 1 < nblk) stage(e + NST - 1, (e + NST - 1) % NST);
+    const char* kt = ring + buf * kIdxTileBytes;
     const bool clip = blk * kBlock + kBlock - 1 > p_first;
     float mx[4];
 #pragma unroll
@@ -260,25 +293,21 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
           *reinterpret_cast<f32x4*>(p.scores + (size_t)orow[ct] * p.score_stride + (blk & ~15) + 4 * g) =
               f32x4{win[ct][0], win[ct][1], win[ct][2], win[ct][3]};
     }
-    if (more) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int cidx = tid + 256 * k;
-        *reinterpret_cast<u32x4*>(lds[buf ^ 1] + k_off(cidx >> 4, cidx & 15)) = stage[k];
-      }
-    }
   }
+  // every wave is done with the ring before the next tile's DMAs start
+  __syncthreads();
 }
 
+template <int NST>
 __global__ __launch_bounds__(256) void indexer_score_prefill_kernel(IndexerParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[2][kBlock * 256];
+  __shared__ __attribute__((aligned(16))) char ring[NST * kIdxTileBytes];
   __shared__ int item_s;
   extern __shared__ int32_t pages_lds[];   // page ids of the tile's block range
   for (;;) {
     const int k = take_item(p.sched, &item_s);
     if (k < 0) break;
     const IdxTile T = idx_tile_of(p, p.worklist[k]);
-    indexer_prefill_tile(p, T, lds, pages_lds);
+    indexer_prefill_tile<NST>(p, T, ring, pages_lds);
   }
 }
 
@@ -289,9 +318,17 @@ hipError_t launch_indexer_prefill(const IndexerParams& p, int num_cus, hipStream
                      (size_t)(p.nbmax + 1) * sizeof(int), s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // two 64 KiB workgroups fit in a CU's LDS
-  hipLaunchKernelGGL(indexer_score_prefill_kernel, dim3(2 * num_cus), dim3(256),
-                     (size_t)p.nbmax * sizeof(int32_t), s, p);
+  // Two workgroups per CU with two-stage rings when both fit in 160 KiB of
+  // LDS (two waves per SIMD hide each other's LDS and MFMA latencies);
+  // otherwise one workgroup per CU with a deeper ring.
+  const size_t pages = (size_t)p.nbmax * sizeof(int32_t);
+  const size_t lds_cu = 160 * 1024;
+  if (2 * (2 * kIdxTileBytes + pages + 64) <= lds_cu)
+    hipLaunchKernelGGL(indexer_score_prefill_kernel<2>, dim3(2 * num_cus), dim3(256), pages, s, p);
+  else if (4 * kIdxTileBytes + pages + 64 <= lds_cu)
+    hipLaunchKernelGGL(indexer_score_prefill_kernel<4>, dim3(num_cus), dim3(256), pages, s, p);
+  else
+    hipLaunchKernelGGL(indexer_score_prefill_kernel<3>, dim3(num_cus), dim3(256), pages, s, p);
   return hipGetLastError();
 }
 
@@ -401,7 +438,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(3))) char lds_char;
 
 // 8-byte transposing LDS reads of 16-bit and of 8-bit elements
 __device__ __forceinline__ u32x2 lds_tr_b16(const char* p) {
@@ -412,28 +448,6 @@ __device__ __forceinline__ u32x2 lds_tr_b8(const char* p) {
   const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_char*)p);
   return __builtin_bit_cast(u32x2, v);
 }
-
-// Global -> LDS copy of 16 bytes per lane: lane L's bytes land at lds_dst +
-// 16 L (lds_dst is wave-uniform).  Written as inline asm (M0 = LDS address,
-// one wait state, the DMA; no register outputs) rather than the builtin,
-// because the compiler treats a builtin DMA as a pending LDS write and waits
-// for every one of them before any later LDS read, which would drain the
-// tile ring on every block.  The callers order each stage's reads after its
-// DMA themselves: an explicit vmcnt wait for this wave's own DMA, then a
-// workgroup barrier for everyone else's.
-// M0 is reserved to the compiler, which warns about the clobber; nothing in
-// these kernels keeps a value in M0 across a DMA (every M0 write in the
-// generated code is the one above its DMA).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
-  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)(lds_char*)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_addr)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // FP8 tile swizzles (16-byte column XOR masks of row pos)
 __device__ __forceinline__ int fp8_kswz(int pos) { return (pos >> 1) & 7; }
