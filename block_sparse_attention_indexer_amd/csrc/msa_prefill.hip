@@ -405,17 +405,20 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams
 // instruction picks its source so that its fixed LDS slot receives the right
 // swizzled piece.
 //
-// BF16: column c of row pos is stored at c ^ (pos & 15).  The PV A-operand
+// BF16: K column c of row pos is stored at c ^ (pos & 15), V column c at
+// c ^ ((pos & 7) << 1).  The PV A-operand
 // (V^T) comes from two ds_read_b64_tr_b16 per fragment: within each 16-lane
 // group, output lane i, element k is element i % 4 of source lane i / 4 +
 // 4k, so source lane j reads row 16r + 4g + j / 4 at dims 16dt + 4(j % 4),
 // which yields for lane (m, g) the positions 16r + 4g + k of dim 16dt + m --
 // exactly the P^T B-operand layout.
 //
-// FP8 (e4m3, widened to BF16 in registers as operands are read): K column c
-// of row pos sits at c ^ ((pos >> 1) & 7), V column c at c ^ fv(pos) built
-// from bits 1, 4 and 2 of pos; that keeps the 16 rows of a K operand read
-// and the 8 rows of a transposed V read in distinct bank groups.  V^T comes
+// FP8 (e4m3, widened to BF16 in registers as operands are read): K is kept
+// in MFMA fragment order (each operand read is 16 consecutive bytes per
+// lane), V column c of row pos at c ^ fv(pos) built from bits 1, 4 and 2 of
+// pos, which keeps the rows of a transposed V read in distinct bank groups
+// (both layouts measured conflict-free with the LDS bank-conflict counter).
+// V^T comes
 // from one ds_read_b64_tr_b8 per fragment: within each 16-lane group, output
 // lane i, element k is byte i % 8 of source lane i / 8 + 2k, so source lanes
 // 2k and 2k + 1 read the row holding P^T position k at dims 16dt and
@@ -450,7 +453,6 @@ __device__ __forceinline__ u32x2 lds_tr_b8(const char* p) {
 }
 
 // FP8 tile swizzles (16-byte column XOR masks of row pos)
-__device__ __forceinline__ int fp8_kswz(int pos) { return (pos >> 1) & 7; }
 __device__ __forceinline__ int fp8_vswz(int pos) {
   return ((pos >> 1) & 1) | (((pos >> 4) & 1) << 1) | (((pos >> 2) & 1) << 2);
 }
@@ -462,7 +464,7 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   constexpr int TILE = kBlock * RB;         // bytes of one K (or V) tile
   constexpr int NST = kRingBytes / TILE;    // ring stages: 2 (BF16), 4 (FP8)
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform((int)(tid >> 6));
   const int l16 = lane & 15, g = lane >> 4;
   const int h = slot % p.H_kv;
   const int tile = (slot / p.H_kv) % p.ntiles;
@@ -496,7 +498,12 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     plim_col[ct] = ok ? c + t0 + tl_col[ct] : -1;
     const uint16_t* qp = p.q + ((size_t)(r0 + t0 + tl_col[ct]) * p.H_q + h * p.G + cg % p.G) * kDim;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[ct][s] = ok ? ld16(qp + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 4; ++s) {
+      // contraction dims of k-step s for lane group g: BF16 32s + 8g + j;
+      // FP8 (K in fragment order, s = 2h + t) 16g + 64h + 8t + j
+      const int d0 = FP8 ? 16 * g + 64 * (s >> 1) + 8 * (s & 1) : 32 * s + 8 * g;
+      qf[ct][s] = ok ? ld16(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   const int p_wave_min = c + t0 + tok_lo;
 
@@ -516,13 +523,15 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   // ---- lane-constant LDS addresses ---------------------------------------
   // BF16 K A-operand: row 16pt + l16 (+ 64hb), logical column 4s + g
   //   = l16 * 256 + ((4s + g) ^ l16) * 16 = kq ^ (s << 6), kq for s = 0
-  // FP8 K A-operand: row 16pt + l16 (+ 64hb), bytes 32s + 8g.. = logical
-  //   column 2s + g / 2, half g % 2: with x = (g / 2) ^ kswz(l16),
-  //   l16 * 128 + ((2s ^ x) << 4) + 8 (g % 2) = kq ^ (s << 5)
-  const int kq = FP8 ? l16 * 128 + ((((g >> 1) ^ fp8_kswz(l16))) << 4) + 8 * (g & 1)
-                     : l16 * 256 + ((g ^ l16) << 4);
+  // FP8 K is stored in fragment order: fragment f = 2 * (row tile) + h is
+  //   1 KiB where lane (l16, g) holds row 16 * tile + l16, bytes 16g + 64h
+  //   .. + 15 (k-steps 2h and 2h + 1), so an operand read is at f * 1024 +
+  //   16 * lane: linear, hence free of bank conflicts
+  const int kq = FP8 ? 16 * lane : l16 * 256 + ((g ^ l16) << 4);
   // BF16 V^T A-operand (transpose read r of chunk ch, dim tile dt): row
-  //   32ch + 16r + q with q = 4g + l16 / 4, dims 16dt + 4(l16 % 4)
+  //   32ch + 16r + q with q = 4g + l16 / 4, dims 16dt + 4(l16 % 4); V column
+  //   c of row pos is stored at c ^ ((pos & 7) << 1), which puts the 8 rows
+  //   one 32-lane half of a transpose read touches in distinct bank groups
   //   = (32ch + 16r) * 256 + (vq ^ (dt << 5))
   // FP8 V^T A-operand (one transpose read of chunk ch, dim tile dt): source
   //   lane l16 reads P^T position k = l16 / 2, i.e. row
@@ -535,30 +544,47 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     vq = vrow * 128 + (fp8_vswz(vrow) << 4) + 8 * (l16 & 1);
   } else {
     const int vq_row = 4 * g + (l16 >> 2);
-    vq = vq_row * 256 + (((((l16 & 3) >> 1)) ^ vq_row) << 4) + 8 * (l16 & 1);
+    vq = vq_row * 256 + (((((l16 & 3) >> 1)) ^ ((vq_row & 7) << 1)) << 4) + 8 * (l16 & 1);
   }
-  // DMA: instruction i of this wave covers kRowsPerDma rows from
-  // kRowsPerWave * wave + kRowsPerDma * i; a lane lands in row
-  // + lane / (RB / 16) at physical column lane % (RB / 16)
+  // DMA.  Row-major tiles: instruction i of this wave covers kRowsPerDma
+  // rows from kRowsPerWave * wave + kRowsPerDma * i; a lane lands in row
+  // + lane / (RB / 16) at physical column lane % (RB / 16).  FP8 K: one
+  // fragment (1 KiB) per instruction, 16 / kP3Waves of them per wave.
   constexpr int kCols = RB / 16;                      // 16-byte columns per row
   constexpr int kRowsPerDma = 64 / kCols;
   constexpr int kRowsPerWave = kBlock / kP3Waves;     // tile rows each wave fetches
   constexpr int kDmaPerWave = kRowsPerWave / kRowsPerDma;
+  static_assert(!FP8 || 16 % kP3Waves == 0, "FP8 K fragments split evenly over the waves");
+  constexpr int kDmaK = FP8 ? 16 / kP3Waves : kDmaPerWave;
+  constexpr int kDmaV = kDmaPerWave;
   const int dr = lane / kCols, dc = lane % kCols;
   const char* kpool = static_cast<const char*>(p.k.data);
   const char* vpool = static_cast<const char*>(p.v.data);
   const uint32_t kts = (uint32_t)p.k.token_stride * ESZ, vts = (uint32_t)p.v.token_stride * ESZ;
   const size_t khead = (size_t)h * p.k.head_stride * ESZ, vhead = (size_t)h * p.v.head_stride * ESZ;
   const size_t kps = (size_t)p.k.page_stride * ESZ, vps = (size_t)p.v.page_stride * ESZ;
-  // byte offsets (within a tile) of the pieces this lane fetches
-  uint32_t koff[kDmaPerWave], voff[kDmaPerWave];
+  // byte offsets (within a page's tile) of the pieces this lane fetches, and
+  // the LDS offsets (within a stage) of the wave's DMA instructions
+  uint32_t koff[kDmaK], voff[kDmaV];
+  int kdst[kDmaK], vdst[kDmaV];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
+  for (int i = 0; i < kDmaK; ++i) {
+    if constexpr (FP8) {
+      const int f = wave * kDmaK + i;
+      koff[i] = (16 * (f >> 1) + l16) * kts + 16 * g + 64 * (f & 1);
+      kdst[i] = f * 1024;
+    } else {
+      const int row = kRowsPerWave * wave + kRowsPerDma * i + dr;
+      koff[i] = row * kts + ((dc ^ (row & 15)) << 4);
+      kdst[i] = (kRowsPerWave * wave + kRowsPerDma * i) * RB;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaV; ++i) {
     const int row = kRowsPerWave * wave + kRowsPerDma * i + dr;
-    const uint32_t kcol = (FP8 ? dc ^ fp8_kswz(row) : dc ^ (row & 15)) << 4;
-    const uint32_t vcol = (FP8 ? dc ^ fp8_vswz(row) : dc ^ (row & 15)) << 4;
-    koff[i] = row * kts + kcol;
+    const uint32_t vcol = (FP8 ? dc ^ fp8_vswz(row) : dc ^ ((row & 7) << 1)) << 4;
     voff[i] = row * vts + vcol;
+    vdst[i] = (kRowsPerWave * wave + kRowsPerDma * i) * RB;
   }
 
   auto stage = [&](int pg, int buf) {
@@ -566,10 +592,9 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     const char* kb = kpool + (size_t)pg * kps + khead;
     const char* vb = vpool + (size_t)pg * vps + vhead;
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      dma16(kb + koff[i], L.k + buf * TILE + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
-      dma16(vb + voff[i], L.v + buf * TILE + (kRowsPerWave * wave + kRowsPerDma * i) * RB);
-    }
+    for (int i = 0; i < kDmaK; ++i) dma16(kb + koff[i], L.k + buf * TILE + kdst[i]);
+#pragma unroll
+    for (int i = 0; i < kDmaV; ++i) dma16(vb + voff[i], L.v + buf * TILE + vdst[i]);
   };
 
   auto ring_fill = [&](int first) {
@@ -598,7 +623,7 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     // this wave's DMA into buf has landed: at most the DMA instructions of
     // the NST - 2 younger blocks may still be in flight (vmcnt counts this
     // wave's vector-memory operations in issue order; lgkm and exp untouched)
-    constexpr int kYounger = 2 * kDmaPerWave * (NST - 2);
+    constexpr int kYounger = (kDmaK + kDmaV) * (NST - 2);
     static_assert(kYounger < 16, "vmcnt immediate holds 4 bits here");
     if (NST > 2 && e + NST - 2 < cnt) __builtin_amdgcn_s_waitcnt(0xF70 | kYounger);
     else __builtin_amdgcn_s_waitcnt(0xF70);
@@ -640,18 +665,23 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
     f32x4 S[kHalves][4][NCT];
     auto qk_half = [&](int hb, f32x4 (&Sh)[4][NCT]) {
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < 4; ++pt) {
+        u32x4 w8 = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           u32x4 a;
-          if constexpr (FP8)
-            a = fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>(kt + (64 * hb + 16 * pt) * RB + (kq ^ (s << 5))));
-          else
+          if constexpr (FP8) {
+            if ((s & 1) == 0)
+              w8 = *reinterpret_cast<const u32x4*>(kt + (2 * (4 * hb + pt) + (s >> 1)) * 1024 + kq);
+            a = fp8x8_to_bf16x8((s & 1) ? u32x2{w8.z, w8.w} : u32x2{w8.x, w8.y});
+          } else {
             a = *reinterpret_cast<const u32x4*>(kt + (64 * hb + 16 * pt) * RB + (kq ^ (s << 6)));
+          }
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct)
             Sh[pt][ct] = mfma_bf16(a, qf[ct][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : Sh[pt][ct]);
         }
+      }
     };
     if constexpr (kHalves == 2) {
       qk_half(0, S[0]);
