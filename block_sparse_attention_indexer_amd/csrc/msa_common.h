@@ -74,14 +74,25 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t x, uint32_t y, int odd)
 }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the four row groups of
-// an MFMA C tile that share a column).
-__device__ __forceinline__ float colgroup_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// an MFMA C tile that share a column), with the gfx950 VALU lane swaps:
+// v_permlane16_swap(x, x) leaves {x[l], x[l ^ 16]} in its two results (in
+// either order, measured on every lane) and v_permlane32_swap likewise
+// {x[l], x[l ^ 32]}, so one max or add of the pair is a butterfly step --
+// a few cycles, where a cross-row shuffle would go through the LDS crossbar.
+__device__ __forceinline__ float xor16_max(float x) {
+  const u32x2 s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
 }
+__device__ __forceinline__ float xor32_max(float x) {
+  const u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s.x), __uint_as_float(s.y));
+}
+__device__ __forceinline__ float colgroup_max(float x) { return xor32_max(xor16_max(x)); }
 __device__ __forceinline__ float colgroup_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a.x) + __uint_as_float(a.y);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b.x) + __uint_as_float(b.y);
 }
 
 // Order-preserving map float -> uint32 (larger float, larger key); -0 and +0

@@ -611,44 +611,64 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   ring_fill(0);
   ring_fill(kRingHalf);
   __syncthreads();
-  // the first NST - 1 blocks are requested up front; block e + NST - 1 is
-  // requested once block e's barrier shows that every wave is done with the
-  // stage it reuses
+  // Blocks go through the ring in groups of SYNC = NST / 2 (one group of
+  // stages being computed while the next is in flight).  The first NST -
+  // SYNC blocks are requested up front.  At the start of each group every
+  // wave waits for its own DMAs, then all meet at a barrier; the group's
+  // blocks are then computed with no barrier between them (waves drift
+  // apart by up to a group, which evens out which SIMDs have work), and the
+  // blocks NST - SYNC ahead are requested into the stages the previous group
+  // released.
+  constexpr int SYNC = NST / 2;
 #pragma unroll
-  for (int j = 0; j < NST - 1; ++j)
+  for (int j = 0; j < NST - SYNC; ++j)
     if (j < cnt) stage(L.ring_pg[j], j);
 
   for (int e = 0; e < cnt; ++e) {
     const int buf = e % NST;
-    // this wave's DMA into buf has landed: at most the DMA instructions of
-    // the NST - 2 younger blocks may still be in flight (vmcnt counts this
-    // wave's vector-memory operations in issue order; lgkm and exp untouched)
-    constexpr int kYounger = (kDmaK + kDmaV) * (NST - 2);
-    static_assert(kYounger < 16, "vmcnt immediate holds 4 bits here");
-    if (NST > 2 && e + NST - 2 < cnt) __builtin_amdgcn_s_waitcnt(0xF70 | kYounger);
-    else __builtin_amdgcn_s_waitcnt(0xF70);
-    // ... and every other wave's.  A bare barrier: a fenced one would also
-    // wait for the younger DMAs still in flight.  Nothing before it needs
-    // ordering: LDS traffic of block e - 1 was consumed by this wave's MFMAs,
-    // and the ring and zeroing writes have barriers of their own.
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_s_barrier();
-    if (e >= kRingHalf && (e & (kRingHalf - 1)) == 0) ring_fill(e + kRingHalf);
+    if (e % SYNC == 0) {
+      // every DMA this wave issued is for blocks e .. e + NST - SYNC - 1; the
+      // group's own blocks are the oldest SYNC of them and the rest
+      // (NST - 2 SYNC blocks) may stay in flight
+      constexpr int kYounger = (kDmaK + kDmaV) * (NST - 2 * SYNC);
+      static_assert(kYounger < 16, "vmcnt immediate holds 4 bits here");
+      if (kYounger > 0 && e + NST - SYNC <= cnt) __builtin_amdgcn_s_waitcnt(0xF70 | kYounger);
+      else __builtin_amdgcn_s_waitcnt(0xF70);
+      // ... and every other wave's.  A bare barrier: a fenced one would also
+      // wait for the younger DMAs still in flight.  Nothing before it needs
+      // ordering: LDS traffic of earlier blocks was consumed by this wave's
+      // MFMAs, and the ring and zeroing writes have barriers of their own.
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_s_barrier();
+      if (e >= kRingHalf && (e & (kRingHalf - 1)) == 0) ring_fill(e + kRingHalf);
+      // V rows past every token of the tile hold no data: zero them (only
+      // the tile's last block can have such rows) so that a zero
+      // probability never meets a NaN
+      bool zeroed = false;
+#pragma unroll
+      for (int j = 0; j < SYNC; ++j) {
+        if (e + j >= cnt) break;
+        const int bj = uniform(L.ring_blk[(e + j) & (2 * kRingHalf - 1)]);
+        if (bj * kBlock + kBlock - 1 > p_tile_max) {
+          for (int i = tid; i < kBlock * kCols; i += kP3Waves * 64) {
+            const int row = i / kCols;
+            if (bj * kBlock + row > p_tile_max)
+              *reinterpret_cast<u32x4*>(L.v + ((e + j) % NST) * TILE + row * RB + (i % kCols) * 16) =
+                  u32x4{0u, 0u, 0u, 0u};
+          }
+          zeroed = true;
+        }
+      }
+      if (zeroed) __syncthreads();
+#pragma unroll
+      for (int j = 0; j < SYNC; ++j) {
+        const int ej = e + NST - SYNC + j;
+        if (ej < cnt) stage(L.ring_pg[ej & (2 * kRingHalf - 1)], ej % NST);
+      }
+    }
     const int rc = e & (2 * kRingHalf - 1);
     const int blk = uniform(L.ring_blk[rc]);
     const uint32_t msk = uniform(L.ring_msk[rc]);
-    // V rows past every token of the tile hold no data: zero them (only the
-    // tile's last block can have such rows) so that a zero probability never
-    // meets a NaN
-    if (blk * kBlock + kBlock - 1 > p_tile_max) {
-      for (int i = tid; i < kBlock * kCols; i += kP3Waves * 64) {
-        const int row = i / kCols;
-        if (blk * kBlock + row > p_tile_max)
-          *reinterpret_cast<u32x4*>(L.v + buf * TILE + row * RB + (i % kCols) * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();
-    }
-    if (e + NST - 1 < cnt) stage(L.ring_pg[(e + NST - 1) & (2 * kRingHalf - 1)], (e + NST - 1) % NST);
     if (!(msk & wave_bits)) continue;
 
     const bool diag = blk * kBlock + kBlock - 1 > p_wave_min;
