@@ -15,6 +15,9 @@ It is written from the method's statement on these pages:
   ordinary masked pass over the selected positions.
 * "ferrox_core::block_sparse", section "The block size is an ABI, not a
   tuning knob": blocks are 128 tokens and coincide with KV pages.
+* "DeepSeekSparseAttentionConfig" (TensorRT-LLM API reference), field
+  ``indexer_k_dtype``: an FP8 index-K cache holds one e4m3 code per element
+  and one float32 scale per 128 elements (per token at head dim 128).
 * "msa" (MAX Mojo module docs, graph-op bindings for the MiniMax-M3 MSA
   kernels), intro and routes paragraphs: BF16 index-K, BF16 or scale-free FP8
   e4m3 main KV, FP32 accumulation, a token's position is its sequence's cache
@@ -109,6 +112,14 @@ def forced_blocks(nb: int, init_blocks: int, local_blocks: int) -> list:
     first = set(range(0, min(init_blocks, nb)))
     newest = set(range(max(0, nb - local_blocks), nb))
     return sorted(first | newest)
+
+
+def index_k_values(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """FP8 index-K ("DeepSeekSparseAttentionConfig" page, indexer_k_dtype):
+    one e4m3 code per element and one float32 scale per token; the value is
+    code * scale.  codes [n, D] raw e4m3 bits, scales [n] float32; the
+    products are exact in float64."""
+    return decode_e4m3fn(codes).astype(np.float64) * scales.astype(np.float64)[:, None]
 
 
 def position_scores(q_idx: np.ndarray, ik_rows: np.ndarray) -> np.ndarray:
@@ -236,6 +247,8 @@ class Problem:
     init_blocks: int
     local_blocks: int
     scale: float
+    ik_dtype: str = "bf16"        # index-K: "bf16", or "fp8_e4m3" codes + scales
+    index_k_scale: np.ndarray = None   # float32 [P, H_ik, 128] for FP8 index-K
 
     @property
     def num_kv_heads(self):
@@ -281,9 +294,18 @@ def select_row(pb: Problem, r: int) -> list:
     cands = [blk for blk in range(nb) if blk not in F]
     sels = [None] * H_kv
     for hk in range(H_ik):
-        rows = decode_bf16(gather_rows(pb.index_k, pb.kv_lookup_table[b], hk, p + 1))
+        codes = gather_rows(pb.index_k, pb.kv_lookup_table[b], hk, p + 1)
+        if pb.ik_dtype == "fp8_e4m3":
+            sc = gather_rows(pb.index_k_scale[..., None], pb.kv_lookup_table[b], hk, p + 1)[:, 0]
+            rows = index_k_values(codes, sc)
+        else:
+            rows = decode_bf16(codes)
         for h in range(hk, H_kv, H_ik):
-            s = position_scores(decode_bf16(pb.q_idx[r, h]), rows)
+            if pb.ik_dtype == "fp8_e4m3":
+                # values are no longer BF16-exact: score in float64
+                s = rows @ decode_bf16(pb.q_idx[r, h]).astype(np.float64)
+            else:
+                s = position_scores(decode_bf16(pb.q_idx[r, h]), rows)
             sels[h] = block_sparse_select(nb, block_scores(s, p, cands), pb.top_k,
                                           pb.init_blocks, pb.local_blocks)
     return sels
@@ -352,6 +374,9 @@ def problem_from_inputs(inp, rows_needed=None) -> Problem:
     return Problem(
         q=bits(inp.q), q_idx=bits(inp.q_idx), index_k=bits(inp.index_k),
         k_cache=bits(inp.k_cache), v_cache=bits(inp.v_cache), kv_dtype=wl.kv_dtype,
+        ik_dtype=wl.ik_dtype,
+        index_k_scale=(None if inp.index_k_scale is None
+                       else inp.index_k_scale.detach().contiguous().cpu().numpy()),
         input_row_offsets=inp.input_row_offsets.cpu().numpy().astype(np.int64),
         cache_lengths=inp.cache_lengths.cpu().numpy().astype(np.int64),
         kv_lookup_table=inp.kv_lookup_table.cpu().numpy().astype(np.int64),
@@ -388,6 +413,9 @@ def problem_for_sequences(inp, seqs) -> tuple:
     pb = Problem(
         q=bits(inp.q[ridx]), q_idx=bits(inp.q_idx[ridx]), index_k=bits(inp.index_k[idx]),
         k_cache=bits(inp.k_cache[idx]), v_cache=bits(inp.v_cache[idx]), kv_dtype=wl.kv_dtype,
+        ik_dtype=wl.ik_dtype,
+        index_k_scale=(None if inp.index_k_scale is None
+                       else inp.index_k_scale[idx].detach().contiguous().cpu().numpy()),
         input_row_offsets=sub_offs, cache_lengths=clen[seqs], kv_lookup_table=sub_table,
         top_k=wl.top_k, init_blocks=wl.init_blocks, local_blocks=wl.local_blocks,
         scale=wl.softmax_scale)

@@ -25,8 +25,14 @@ def to_bf16_bits(x):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def fp8_bits(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
 def make_problem(rng, new_lens, cache_lens, H_kv=2, G=2, H_ik=1, D=16, top_k=3,
-                 init=1, local=1, kv_dtype="bf16", extra_pages=3, scale=None, poison=True):
+                 init=1, local=1, kv_dtype="bf16", extra_pages=3, scale=None, poison=True,
+                 ik_dtype="bf16"):
     B = len(new_lens)
     L = [c + n for c, n in zip(cache_lens, new_lens)]
     pages = [(x + BLK - 1) // BLK for x in L]
@@ -53,19 +59,30 @@ def make_problem(rng, new_lens, cache_lens, H_kv=2, G=2, H_ik=1, D=16, top_k=3,
         k = f8(P, H_kv, BLK, D)
         v = f8(P, H_kv, BLK, D)
     ik = bf(P, H_ik, BLK, D)
+    ik_scale = None
+    if ik_dtype == "fp8_e4m3":
+        # codes of N(0,1) values with one scale per token, max |value| -> 448
+        vals = rng.standard_normal((P, H_ik, BLK, D)).astype(np.float32)
+        ik_scale = (np.abs(vals).max(axis=-1) / 448.0).astype(np.float32)
+        ik = fp8_bits(vals / ik_scale[..., None])
     if poison:
         nan16 = np.uint16(0x7FC0)
         nan8 = np.uint8(0x7F)
         used = set(table[b, i] for b in range(B) for i in range(pages[b]))
+        nan_ik = nan8 if ik_dtype == "fp8_e4m3" else nan16
         for pg in range(P):
             if pg not in used:
-                ik[pg] = nan16
+                ik[pg] = nan_ik
+                if ik_scale is not None:
+                    ik_scale[pg] = np.nan
                 k[pg] = nan16 if kv_dtype == "bf16" else nan8
                 v[pg] = nan16 if kv_dtype == "bf16" else nan8
         for b in range(B):
             if L[b] % BLK:
                 pg = table[b, pages[b] - 1]
-                ik[pg, :, L[b] % BLK:] = nan16
+                ik[pg, :, L[b] % BLK:] = nan_ik
+                if ik_scale is not None:
+                    ik_scale[pg, :, L[b] % BLK:] = np.nan
                 k[pg, :, L[b] % BLK:] = nan16 if kv_dtype == "bf16" else nan8
                 v[pg, :, L[b] % BLK:] = nan16 if kv_dtype == "bf16" else nan8
     offs = np.zeros(B + 1, dtype=np.int64)
@@ -74,7 +91,8 @@ def make_problem(rng, new_lens, cache_lens, H_kv=2, G=2, H_ik=1, D=16, top_k=3,
                      v_cache=v, kv_dtype=kv_dtype, input_row_offsets=offs,
                      cache_lengths=np.asarray(cache_lens, dtype=np.int64),
                      kv_lookup_table=table, top_k=top_k, init_blocks=init,
-                     local_blocks=local, scale=(1 / math.sqrt(D)) if scale is None else scale)
+                     local_blocks=local, scale=(1 / math.sqrt(D)) if scale is None else scale,
+                     ik_dtype=ik_dtype, index_k_scale=ik_scale)
 
 
 def logical(pb, pool, b, h, n):
@@ -159,7 +177,12 @@ def brute_force(pb):
             p = c + t
             nb = p // BLK + 1
             for h in range(H_kv):
-                ik = O.decode_bf16(logical(pb, pb.index_k, b, h % H_ik, L)).astype(np.float64)
+                if pb.ik_dtype == "fp8_e4m3":
+                    codes = O.decode_e4m3fn(logical(pb, pb.index_k, b, h % H_ik, L)).astype(np.float64)
+                    scl = logical(pb, pb.index_k_scale[..., None], b, h % H_ik, L)[:, 0]
+                    ik = np.array([[codes[j, d] * float(scl[j]) for d in range(D)] for j in range(L)])
+                else:
+                    ik = O.decode_bf16(logical(pb, pb.index_k, b, h % H_ik, L)).astype(np.float64)
                 qi = O.decode_bf16(pb.q_idx[r, h]).astype(np.float64)
                 score = {}
                 for blk in range(nb):
@@ -221,6 +244,73 @@ def test_brute_force_tiny_separate_index_heads():
     d, _ = O.indexer(pb)
     for (r, h), S in sels.items():
         assert [x for x in d[r, h] if x >= 0] == S
+
+
+@pytest.mark.parametrize("seed,H_ik", [(21, 1), (22, 2)])
+def test_brute_force_tiny_fp8_index_k(seed, H_ik):
+    rng = np.random.default_rng(seed)
+    pb = make_problem(rng, new_lens=[1, 3], cache_lens=[700, 260], H_kv=2, G=2, H_ik=H_ik,
+                      D=8, top_k=3, init=1, local=1, ik_dtype="fp8_e4m3")
+    sels, _ = brute_force(pb)
+    d, _ = O.indexer(pb)
+    for (r, h), S in sels.items():
+        assert [x for x in d[r, h] if x >= 0] == S, (r, h)
+
+
+# ---------------------------------------------------------------------------
+# FP8 index-K: codes times a per-token scale
+# ---------------------------------------------------------------------------
+
+def test_fp8_index_k_with_power_of_two_scales_equals_bf16_values():
+    # e4m3 values times 2^e are BF16-exact: the FP8 path must then select
+    # exactly what the BF16 path selects on those values
+    rng = np.random.default_rng(31)
+    pb8 = make_problem(rng, new_lens=[1, 2], cache_lens=[2500, 1800], H_kv=2, G=2, D=16,
+                       top_k=5, init=1, local=1, ik_dtype="fp8_e4m3", poison=False)
+    P, H_ik = pb8.index_k.shape[:2]
+    pb8.index_k = fp8_bits(rng.standard_normal(pb8.index_k.shape) * 8)
+    pb8.index_k_scale = (2.0 ** rng.integers(-6, 4, size=(P, H_ik, BLK))).astype(np.float32)
+    vals = O.decode_e4m3fn(pb8.index_k).astype(np.float64) * pb8.index_k_scale[..., None]
+    bits = to_bf16_bits(vals)
+    assert (O.decode_bf16(bits).astype(np.float64) == vals).all()      # exact
+    pb16 = O.Problem(**{**pb8.__dict__, "index_k": bits, "ik_dtype": "bf16", "index_k_scale": None})
+    d8, s8 = O.indexer(pb8)
+    d16, s16 = O.indexer(pb16)
+    n = 0
+    for i in range(d8.shape[0]):
+        for h in range(d8.shape[1]):
+            if s8[i][h].decisive and s16[i][h].decisive:
+                assert (d8[i, h] == d16[i, h]).all()
+                n += 1
+    assert n >= d8.shape[0] * d8.shape[1] - 1
+
+
+def test_fp8_index_k_needle_through_the_scale_alone():
+    # one position's codes are ordinary; only its scale is raised -- the
+    # score must follow code . q times the scale
+    rng = np.random.default_rng(32)
+    pb = make_problem(rng, new_lens=[1], cache_lens=[24 * BLK - 1], H_kv=2, G=2, D=16,
+                      top_k=4, init=1, local=1, ik_dtype="fp8_e4m3")
+    b, h, target = 0, 0, 13
+    qv = O.decode_bf16(pb.q_idx[0, h])
+    j = target * BLK + 40
+    page = pb.kv_lookup_table[b, j // BLK]
+    pb.index_k[page, 0, j % BLK] = fp8_bits(np.sign(qv) * 64.0)     # aligned with q, |code| 64
+    pb.index_k_scale[page, 0, j % BLK] = 1e3
+    d, _ = O.indexer(pb)
+    assert target in d[0, h]
+
+
+def test_fp8_index_k_common_scale_factor_invariance():
+    rng = np.random.default_rng(33)
+    pb = make_problem(rng, new_lens=[2, 1], cache_lens=[1500, 2600], D=16, top_k=4,
+                      init=1, local=1, ik_dtype="fp8_e4m3")
+    d0, _ = O.indexer(pb)
+    base = pb.index_k_scale.copy()
+    for f in (2.0 ** -5, 2.0 ** 7):
+        pb.index_k_scale = (base * f).astype(np.float32)
+        d1, _ = O.indexer(pb)
+        assert (d0 == d1).all()
 
 
 # ---------------------------------------------------------------------------
