@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch64",
                     help="decode_small | decode_batch64 | spec_decode | prefill_ragged | "
-                         "decode_fp8_long | all")
+                         "decode_fp8_long | decode_fp8_long_fp8ik | all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
@@ -101,7 +101,10 @@ def algorithmic_work(wl, d_idx, rows=None):
             np.maximum.at(cov, np.clip(ids[:, h][m], 0, nbl), vis[:, h][m])
             kv_bytes += int(cov.sum()) * 128 * 2 * esz
         if nbl > wl.top_k:
-            ik_bytes += max(0, nbl - wl.local_blocks - wl.init_blocks) * 128 * 256 * wl.num_ik_heads
+            # bytes per index-K position: 128 BF16 values, or 128 e4m3 codes
+            # plus a float32 scale
+            ik_pos = 132 if wl.ik_dtype == "fp8_e4m3" else 256
+            ik_bytes += max(0, nbl - wl.local_blocks - wl.init_blocks) * 128 * ik_pos * wl.num_ik_heads
             k = np.where(nb > wl.top_k, nb - wl.local_blocks - wl.init_blocks, 0)
             idx_flops += 2 * 128 * wl.num_kv_heads * 128 * int(k.sum())
     return dict(kv_bytes=kv_bytes, ik_bytes=ik_bytes, attn_flops=attn_flops, idx_flops=idx_flops)
@@ -315,7 +318,8 @@ def run(workload, args):
 
     def indexer():
         B.msa_indexer_paged(d, inp.q_idx, inp.index_k, rg, wl.num_kv_heads, wl.top_k,
-                            wl.init_blocks, wl.local_blocks, ws_i, stream)
+                            wl.init_blocks, wl.local_blocks, ws_i, stream,
+                            index_k_scale=inp.index_k_scale)
 
     def attention():
         B.msa_attention_paged(out, inp.q, d, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
@@ -406,7 +410,8 @@ def run(workload, args):
                    "max_context": max(wl.seq_lens()), "kv_heads": wl.num_kv_heads,
                    "gqa": wl.group, "top_k": wl.top_k, "init_blocks": wl.init_blocks,
                    "local_blocks": wl.local_blocks, "kv_dtype": wl.kv_dtype,
-                   "index_k_heads": wl.num_ik_heads, "split_k_partitions": np_},
+                   "index_k_heads": wl.num_ik_heads, "index_k_dtype": wl.ik_dtype,
+                   "split_k_partitions": np_},
         "query_tok_s": tok_s,
         "hbm_frac_of_step": (work["kv_bytes"] + work["ik_bytes"]) / (wall / K) / 1e9 / HBM_PEAK_GBPS,
         "gpu_ms_per_step": gpu_step_ms,
@@ -435,7 +440,8 @@ def main():
     if args.traffic_record:
         write_traffic_record(args)
         return
-    names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long"]
+    names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long",
+              "decode_fp8_long_fp8ik"]
              if args.workload == "all" else [args.workload])
     for name in names:
         print(json.dumps(run(name, args)), flush=True)

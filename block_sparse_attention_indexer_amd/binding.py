@@ -45,6 +45,9 @@ class PagedCache(ctypes.Structure):
         ("page_stride", ctypes.c_int64),
         ("head_stride", ctypes.c_int64),
         ("token_stride", ctypes.c_int64),
+        ("scale", ctypes.c_void_p),
+        ("scale_page_stride", ctypes.c_int64),
+        ("scale_head_stride", ctypes.c_int64),
     ]
 
 
@@ -127,9 +130,11 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def paged_cache(pool: torch.Tensor) -> PagedCache:
+def paged_cache(pool: torch.Tensor, scale: torch.Tensor = None) -> PagedCache:
     """Describe a page pool tensor [pages, heads, 128, 128] (any strides, last
-    dim contiguous) of dtype bfloat16 or float8_e4m3fn."""
+    dim contiguous) of dtype bfloat16 or float8_e4m3fn, and for an FP8
+    index-K cache its per-token scales, float32 [pages, heads, 128] with a
+    contiguous last dim."""
     if pool.dim() != 4 or pool.stride(3) != 1:
         raise ValueError("page pool must be [pages, heads, 128, 128] with a contiguous last dim")
     if pool.dtype == torch.bfloat16:
@@ -139,8 +144,13 @@ def paged_cache(pool: torch.Tensor) -> PagedCache:
     else:
         raise ValueError(f"unsupported cache dtype {pool.dtype}")
     P, H, S, Dm = pool.shape
+    sp, ss0, ss1 = None, 0, 0
+    if scale is not None:
+        if scale.dtype != torch.float32 or scale.dim() != 3 or scale.stride(2) != 1:
+            raise ValueError("scales must be float32 [pages, heads, 128] with a contiguous last dim")
+        sp, ss0, ss1 = scale.data_ptr(), scale.stride(0), scale.stride(1)
     return PagedCache(pool.data_ptr(), dt, P, H, S, Dm, 0, pool.stride(0), pool.stride(1),
-                      pool.stride(2))
+                      pool.stride(2), sp, ss0, ss1)
 
 
 def ragged(input_row_offsets, cache_lengths, kv_lookup_table, max_seq_length: int,
@@ -184,9 +194,11 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def msa_indexer_paged(d_indices, q_idx, index_k, rg: Ragged, num_kv_heads: int, top_k: int,
-                      init_blocks: int, local_blocks: int, workspace=None, stream=None):
-    """Fill d_indices [rows, H_kv, top_k] (int32) with ascending block ids."""
-    cache = paged_cache(index_k)
+                      init_blocks: int, local_blocks: int, workspace=None, stream=None,
+                      index_k_scale=None):
+    """Fill d_indices [rows, H_kv, top_k] (int32) with ascending block ids.
+    index_k_scale: the per-token scales of an FP8 index-K cache."""
+    cache = paged_cache(index_k, index_k_scale)
     need = msa_indexer_workspace_bytes(rg, num_kv_heads, top_k)
     ws = _workspace(need, q_idx.device, workspace)
     st = library().msa_indexer_paged(_ptr(d_indices), _ptr(q_idx), ctypes.byref(cache),
@@ -239,7 +251,8 @@ def run_indexer(inp, d_indices=None, workspace=None, stream=None):
         d_indices = torch.empty((wl.total_rows, wl.num_kv_heads, wl.top_k), dtype=torch.int32,
                                 device=inp.device)
     return msa_indexer_paged(d_indices, inp.q_idx, inp.index_k, rg, wl.num_kv_heads, wl.top_k,
-                             wl.init_blocks, wl.local_blocks, workspace, stream)
+                             wl.init_blocks, wl.local_blocks, workspace, stream,
+                             index_k_scale=inp.index_k_scale)
 
 
 def run_attention(inp, d_indices, output=None, num_partitions: int = 0, workspace=None,

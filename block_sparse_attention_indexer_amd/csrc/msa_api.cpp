@@ -75,11 +75,12 @@ int check_ragged(const msa_ragged* rg) {
 
 bool empty_batch(const msa_ragged& rg) { return rg.batch == 0 || rg.max_seq_length == 0; }
 
-int check_cache(const msa_paged_cache* c, bool allow_fp8) {
+enum class CacheRole { IndexK, KV };
+
+int check_cache(const msa_paged_cache* c, CacheRole role) {
   if (!c) return MSA_ERR_NULL;
   if (!c->data) return MSA_ERR_NULL;
   if (c->dtype != MSA_DTYPE_BF16 && c->dtype != MSA_DTYPE_FP8_E4M3) return MSA_ERR_DTYPE;
-  if (c->dtype == MSA_DTYPE_FP8_E4M3 && !allow_fp8) return MSA_ERR_DTYPE;
   if (c->page_size != MSA_BLOCK_SIZE || c->head_dim != MSA_HEAD_DIM) return MSA_ERR_SHAPE;
   if (c->num_pages < 1 || c->num_heads < 1) return MSA_ERR_SHAPE;
   const int64_t esz = c->dtype == MSA_DTYPE_BF16 ? 2 : 1;
@@ -89,11 +90,21 @@ int check_cache(const msa_paged_cache* c, bool allow_fp8) {
   if (c->token_stride < MSA_HEAD_DIM) return MSA_ERR_SHAPE;
   // kernels address the rows of one page with 32-bit byte offsets
   if (c->token_stride * esz * MSA_BLOCK_SIZE > (int64_t)INT32_MAX) return MSA_ERR_SHAPE;
+  // per-token scales: exactly the FP8 index-K cache has them
+  const bool scaled = role == CacheRole::IndexK && c->dtype == MSA_DTYPE_FP8_E4M3;
+  if (!scaled && c->scale) return MSA_ERR_DTYPE;
+  if (scaled) {
+    if (!c->scale) return MSA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(c->scale) % 16) return MSA_ERR_SHAPE;
+    for (int64_t st : {c->scale_page_stride, c->scale_head_stride})
+      if (st < 0 || st % 4) return MSA_ERR_SHAPE;
+  }
   return MSA_OK;
 }
 
 Pool pool_of(const msa_paged_cache& c) {
-  return Pool{c.data, c.page_stride, c.head_stride, c.token_stride, c.num_pages};
+  return Pool{c.data, c.page_stride, c.head_stride, c.token_stride, c.num_pages,
+              c.scale, c.scale_page_stride, c.scale_head_stride};
 }
 
 Ragged ragged_of(const msa_ragged& rg) {
@@ -237,7 +248,7 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   if ((st = check_selection(top_k, init_blocks, local_blocks)) != MSA_OK) return st;
   if (num_kv_heads < 1) return MSA_ERR_SHAPE;
   if (empty_batch(*rg)) return MSA_OK;   // no rows: buffers may be empty (null)
-  if ((st = check_cache(index_k, false)) != MSA_OK) return st;
+  if ((st = check_cache(index_k, CacheRole::IndexK)) != MSA_OK) return st;
   if (index_k->num_heads != 1 && index_k->num_heads != num_kv_heads) return MSA_ERR_SHAPE;
   if (!d_indices || !q_idx) return MSA_ERR_NULL;
   if (!aligned16(q_idx) || !aligned16(d_indices)) return MSA_ERR_SHAPE;
@@ -249,6 +260,7 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   IndexerParams p{};
   p.q_idx = static_cast<const uint16_t*>(q_idx);
   p.ik = pool_of(*index_k);
+  p.ik_fp8 = index_k->dtype == MSA_DTYPE_FP8_E4M3;
   p.rg = ragged_of(*rg);
   p.scores = static_cast<float*>(workspace);
   p.d_indices = d_indices;
@@ -314,8 +326,8 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   if (num_partitions < 0 || num_partitions > kMaxPartitions) return MSA_ERR_PARAM;
   if (!(scale > 0.f) || scale > 3.0e38f) return MSA_ERR_PARAM;   // positive and finite
   if (empty_batch(*rg)) return MSA_OK;   // no rows: buffers may be empty (null)
-  if ((st = check_cache(k_cache, true)) != MSA_OK) return st;
-  if ((st = check_cache(v_cache, true)) != MSA_OK) return st;
+  if ((st = check_cache(k_cache, CacheRole::KV)) != MSA_OK) return st;
+  if ((st = check_cache(v_cache, CacheRole::KV)) != MSA_OK) return st;
   if (k_cache->dtype != v_cache->dtype) return MSA_ERR_DTYPE;
   if (k_cache->num_heads != num_kv_heads || v_cache->num_heads != num_kv_heads) return MSA_ERR_SHAPE;
   if (k_cache->num_pages != v_cache->num_pages) return MSA_ERR_SHAPE;

@@ -74,7 +74,7 @@ __device__ __forceinline__ int64_t group_units(const IndexerParams& p, int n, in
   return u;
 }
 
-template <int NCT>
+template <int NCT, bool FP8>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParams p, int ncg) {
   __shared__ int64_t chunk_pre[kIdxThreads + 1];
   const int lane = threadIdx.x & 63;
@@ -112,10 +112,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
   int64_t s = w * base + min(w, rem);
   const int64_t e = s + base + (w < rem ? 1 : 0);
 
+  constexpr int ESZ = FP8 ? 1 : 2;    // bytes per index-K element
+  constexpr int KW = FP8 ? 2 : 4;     // 16-byte loads per lane per position tile
   const char* pool = static_cast<const char*>(p.ik.data);
-  const size_t ts = (size_t)p.ik.token_stride * 2;
-  const size_t ps = (size_t)p.ik.page_stride * 2;
-  const size_t lane_off = (size_t)l16 * ts + (8 * g) * 2;
+  const size_t ts = (size_t)p.ik.token_stride * ESZ;
+  const size_t ps = (size_t)p.ik.page_stride * ESZ;
+  const size_t lane_off = (size_t)l16 * ts + (FP8 ? 32 * g : 16 * g);
 
   while (s < e) {
     // chunk holding unit s: the last j with chunk_pre[j] <= s
@@ -165,7 +167,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
       orow[ct] = ok ? (r0 + t) * p.H_kv + h : 0;
       const uint16_t* qp = p.q_idx + (size_t)orow[ct] * kDim;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) qf[ct][q] = ok ? ld16(qp + 32 * q + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      for (int q = 0; q < 4; ++q) {
+        // contraction dims of k-step q for lane group g: BF16 32q + 8g + j;
+        // FP8 (each lane reads 32 consecutive code bytes) 32g + 8q + j
+        const int d0 = FP8 ? 32 * g + 8 * q : 32 * q + 8 * g;
+        qf[ct][q] = ok ? ld16(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 
     // page ids of the segment's blocks, one per lane; out-of-pool ids read
@@ -173,20 +180,33 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
     int pg_lane = 0;
     if (lane < nblk) pg_lane = p.rg.table[(size_t)b * p.rg.stride + blk_lo + lane];
     if ((unsigned)pg_lane >= (unsigned)p.ik.num_pages) pg_lane = -1;
-    const char* head_base = pool + (size_t)hk * p.ik.head_stride * 2 + lane_off;
+    const char* head_base = pool + (size_t)hk * p.ik.head_stride * ESZ + lane_off;
+    const float* scale_head = FP8 ? p.ik.scale + (size_t)hk * p.ik.scale_head_stride : nullptr;
 
-    auto load_half = [&](int u, u32x4 (&kf)[4][4]) {
+    // One 64-position half tile: BF16 as 4 position tiles x 4 k-steps of
+    // MFMA operands; FP8 as 4 position tiles x 32 code bytes (two loads)
+    // plus the scales of the 4 C-tile rows this lane holds per position tile.
+    struct Half {
+      u32x4 k[4][KW];
+      f32x4 sc[FP8 ? 4 : 1];
+    };
+    auto load_half = [&](int u, Half& hf) {
       int pg = __builtin_amdgcn_readlane(pg_lane, u >> 1);
       if (pg < 0) pg = 0;
       const char* src = head_base + (size_t)pg * ps + (size_t)(64 * (u & 1)) * ts;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) kf[pt][q] = ld16(src + (size_t)(16 * pt) * ts + 64 * q);
+        for (int q = 0; q < KW; ++q) hf.k[pt][q] = ld16(src + (size_t)(16 * pt) * ts + (FP8 ? 16 : 64) * q);
+      if constexpr (FP8) {
+        const float* sp = scale_head + (size_t)pg * p.ik.scale_page_stride + 64 * (u & 1) + 4 * g;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) hf.sc[pt] = *reinterpret_cast<const f32x4*>(sp + 16 * pt);
+      }
     };
 
     float mx[NCT];
-    auto compute_half = [&](int u, const u32x4 (&kf)[4][4]) {
+    auto compute_half = [&](int u, const Half& hf) {
       const int blk = blk_lo + (u >> 1);
       const int pos_base = blk * kBlock + 64 * (u & 1);
       const bool clip = pos_base + 63 > c;   // some position past a token
@@ -196,11 +216,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
       }
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
+        u32x4 kf[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (FP8) {
+            const u32x4 w = hf.k[pt][q >> 1];
+            kf[q] = fp8x8_to_bf16x8((q & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y});
+          } else {
+            kf[q] = hf.k[pt][q];
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc4 = mfma_bf16(kf[pt][q], qf[ct][q], acc4);
+          for (int q = 0; q < 4; ++q) acc4 = mfma_bf16(kf[q], qf[ct][q], acc4);
+          // FP8: row i of this C tile is position 16 pt + 4 g + i, whose
+          // value is code * scale, so its dot product is scaled here
+          if constexpr (FP8) acc4 = acc4 * hf.sc[pt];
           if (clip) {
             const int lim = plim[ct] - (pos_base + 16 * pt + 4 * g);
 #pragma unroll
@@ -221,7 +254,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
     };
 
     // halves 0 .. 2 nblk - 1 with the next one always in flight
-    u32x4 kA[4][4], kB[4][4];
+    Half kA, kB;
     load_half(0, kA);
     for (int j = 0; j < nblk; ++j) {
       load_half(2 * j + 1, kB);
@@ -232,18 +265,25 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
   }
 }
 
-// Waves the scorer keeps resident per CU (register-limited occupancy).
-constexpr int score_waves_per_cu(int nct) { return nct >= 4 ? 4 : 8; }
+// Waves the scorer keeps resident per CU (register-limited occupancy; the
+// equal shares assume every wave of the grid is resident at once).
+constexpr int score_waves_per_cu(int nct, bool fp8) { return nct >= 4 ? 4 : (fp8 && nct == 1) ? 12 : 8; }
 
 hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_t s) {
   const int hpi = p.H_kv / p.H_ik;
   const int cols = p.rg.max_seq * hpi;
   const int nct = cols <= 16 ? 1 : cols <= 32 ? 2 : 4;
   const int ncg = (cols + 16 * nct - 1) / (16 * nct);
-  dim3 grid(num_cus * score_waves_per_cu(nct) / kIdxWaves);
-  if (nct == 1) hipLaunchKernelGGL(indexer_score_kernel<1>, grid, dim3(kIdxThreads), 0, s, p, ncg);
-  else if (nct == 2) hipLaunchKernelGGL(indexer_score_kernel<2>, grid, dim3(kIdxThreads), 0, s, p, ncg);
-  else hipLaunchKernelGGL(indexer_score_kernel<4>, grid, dim3(kIdxThreads), 0, s, p, ncg);
+  dim3 grid(num_cus * score_waves_per_cu(nct, p.ik_fp8 != 0) / kIdxWaves);
+  if (p.ik_fp8) {
+    if (nct == 1) hipLaunchKernelGGL((indexer_score_kernel<1, true>), grid, dim3(kIdxThreads), 0, s, p, ncg);
+    else if (nct == 2) hipLaunchKernelGGL((indexer_score_kernel<2, true>), grid, dim3(kIdxThreads), 0, s, p, ncg);
+    else hipLaunchKernelGGL((indexer_score_kernel<4, true>), grid, dim3(kIdxThreads), 0, s, p, ncg);
+  } else {
+    if (nct == 1) hipLaunchKernelGGL((indexer_score_kernel<1, false>), grid, dim3(kIdxThreads), 0, s, p, ncg);
+    else if (nct == 2) hipLaunchKernelGGL((indexer_score_kernel<2, false>), grid, dim3(kIdxThreads), 0, s, p, ncg);
+    else hipLaunchKernelGGL((indexer_score_kernel<4, false>), grid, dim3(kIdxThreads), 0, s, p, ncg);
+  }
   return hipGetLastError();
 }
 

@@ -7,11 +7,14 @@
 
 namespace msa {
 
-// A paged cache as the kernels see it: base pointer and element strides.
+// A paged cache as the kernels see it: base pointer and element strides,
+// plus the per-token scales of an FP8 index-K cache (null otherwise).
 struct Pool {
   const void* data;
   int64_t page_stride, head_stride, token_stride;  // elements
   int32_t num_pages;
+  const float* scale;                               // [page][head][128 slots]
+  int64_t scale_page_stride, scale_head_stride;     // floats
 };
 
 // The ragged batch.
@@ -26,7 +29,8 @@ struct Ragged {
 
 struct IndexerParams {
   const uint16_t* q_idx;  // bf16 [R][H_kv][128]
-  Pool ik;                // bf16, H_ik heads
+  Pool ik;                // H_ik heads: bf16, or fp8 e4m3 codes + per-token scales
+  int32_t ik_fp8;         // 1: FP8 index-K
   Ragged rg;
   float* scores;          // [rcap][H_kv][score_stride]
   int32_t* d_indices;     // [R][H_kv][top_k]

@@ -178,10 +178,17 @@ __global__ __launch_bounds__(kSchedThreads) void indexer_schedule_kernel(Indexer
 }
 
 constexpr int kIdxTileBytes = kBlock * 256;   // one BF16 index-K tile
+// One FP8 index-K stage: 16 fragments of 1 KiB (fragment 2 pt + h: lane
+// (l16, g) holds row 16 pt + l16, code bytes 16 g + 64 h .. + 15, i.e. the
+// k-steps 2h and 2h + 1), then the tile's 128 float32 scales.
+constexpr int kIdxStageFp8 = kBlock * 128 + kBlock * 4;
 
-template <int NST>
+template <int NST, bool FP8>
 __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, char* ring,
                                      int32_t* pages_lds) {
+  constexpr int STAGE = FP8 ? kIdxStageFp8 : kIdxTileBytes;
+  constexpr int ESZ = FP8 ? 1 : 2;                  // bytes per index-K element
+  constexpr int kDmaPerBlock = FP8 ? 5 : 8;         // DMA instructions per wave per tile
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform((int)(tid >> 6));
   const int l16 = lane & 15, g = lane >> 4;
@@ -201,14 +208,19 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
     orow[ct] = ok ? (T.r0 + T.t0 + t) * p.H_kv + h : 0;
     const uint16_t* qp = p.q_idx + (size_t)orow[ct] * kDim;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[ct][s] = ok ? ld16(qp + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 4; ++s) {
+      // contraction dims of k-step s for lane group g: BF16 32s + 8g + j;
+      // FP8 (fragment order) 16g + 64 (s / 2) + 8 (s % 2) + j
+      const int d0 = FP8 ? 16 * g + 64 * (s >> 1) + 8 * (s & 1) : 32 * s + 8 * g;
+      qf[ct][s] = ok ? ld16(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   const int p_first = T.c + T.t0;
 
   const char* pool = static_cast<const char*>(p.ik.data);
-  const uint32_t ts = (uint32_t)p.ik.token_stride * 2;
-  const size_t head_bytes = (size_t)T.hk * p.ik.head_stride * 2;
-  const size_t page_bytes = (size_t)p.ik.page_stride * 2;
+  const uint32_t ts = (uint32_t)p.ik.token_stride * ESZ;
+  const size_t head_bytes = (size_t)T.hk * p.ik.head_stride * ESZ;
+  const size_t page_bytes = (size_t)p.ik.page_stride * ESZ;
   const int32_t* trow = p.rg.table + (size_t)T.b * p.rg.stride;
   const int npages = p.ik.num_pages;
   // The page ids of the whole block range go to LDS first, so the loop
@@ -216,21 +228,36 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
   for (int i = tid; i < nblk; i += 256) pages_lds[i] = trow[blk_lo + i];
   __syncthreads();
 
-  // DMA: instruction i of this wave fills tile rows 32 wave + 4i .. + 3; a
-  // lane lands in row + lane / 16 at physical column lane % 16 and fetches
-  // the logical column that the swizzle puts there.
-  uint32_t doff[8];
+  // DMA.  BF16: instruction i of this wave fills tile rows 32 wave + 4i ..
+  // + 3; a lane lands in row + lane / 16 at physical column lane % 16 and
+  // fetches the logical column that the swizzle puts there.  FP8: the wave
+  // fills fragments 4 wave + i (i < 4), and its lanes 0..7 fetch scales
+  // 32 wave .. + 31.
+  constexpr int kDmaK = FP8 ? 4 : 8;
+  uint32_t doff[kDmaK];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * wave + 4 * i + (lane >> 4);
-    doff[i] = row * ts + ((((lane & 15) ^ (row & 15))) << 4);
+  for (int i = 0; i < kDmaK; ++i) {
+    if constexpr (FP8) {
+      const int f = 4 * wave + i;
+      doff[i] = (16 * (f >> 1) + l16) * ts + 16 * g + 64 * (f & 1);
+    } else {
+      const int row = 32 * wave + 4 * i + (lane >> 4);
+      doff[i] = row * ts + ((((lane & 15) ^ (row & 15))) << 4);
+    }
   }
   auto stage = [&](int rel, int buf) {
     int pg = pages_lds[rel];
     if ((unsigned)pg >= (unsigned)npages) pg = 0;
     const char* kb = pool + (size_t)pg * page_bytes + head_bytes;
+    char* st = ring + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(kb + doff[i], ring + buf * kIdxTileBytes + (32 * wave + 4 * i) * 256);
+    for (int i = 0; i < kDmaK; ++i)
+      dma16(kb + doff[i], st + (FP8 ? (4 * wave + i) * 1024 : (32 * wave + 4 * i) * 256));
+    if constexpr (FP8) {
+      const float* sb = p.ik.scale + (size_t)pg * p.ik.scale_page_stride +
+                        (size_t)T.hk * p.ik.scale_head_stride + 32 * wave;
+      if (lane < 8) dma16(reinterpret_cast<const char*>(sb + 4 * lane), st + kBlock * 128 + 128 * wave);
+    }
   };
 #pragma unroll
   for (int j = 0; j < NST - 1; ++j)
@@ -247,12 +274,12 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
     const int buf = e % NST;
     // this wave's DMA of block e has landed (the 8 DMA instructions of each
     // younger block may still be in flight), then everyone's has
-    if (NST > 2 && e + NST - 2 < nblk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * (NST - 2)));
+    if (NST > 2 && e + NST - 2 < nblk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerBlock * (NST - 2)));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     if (e + NST - 1 < nblk) stage(e + NST - 1, (e + NST - 1) % NST);
-    const char* kt = ring + buf * kIdxTileBytes;
+    const char* kt = ring + buf * STAGE;
     const bool clip = blk * kBlock + kBlock - 1 > p_first;
     float mx[4];
 #pragma unroll
@@ -260,12 +287,26 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
 #pragma unroll 2
     for (int pt = 0; pt < 8; ++pt) {
       f32x4 acc[4];
+      u32x4 w8 = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = lds16(kt, k_off(16 * pt + l16, 4 * s + g));
+        u32x4 a;
+        if constexpr (FP8) {
+          if ((s & 1) == 0) w8 = lds16(kt, (2 * pt + (s >> 1)) * 1024 + 16 * lane);
+          a = fp8x8_to_bf16x8((s & 1) ? u32x2{w8.z, w8.w} : u32x2{w8.x, w8.y});
+        } else {
+          a = lds16(kt, k_off(16 * pt + l16, 4 * s + g));
+        }
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
           acc[ct] = mfma_bf16(a, qf[ct][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[ct]);
+      }
+      if constexpr (FP8) {
+        // rows 4g .. 4g + 3 of this C tile are positions 16 pt + 4g + i:
+        // value = code * scale, so each row's dot product takes its scale
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(kt + kBlock * 128 + (16 * pt + 4 * g) * 4);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = acc[ct] * sc;
       }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
@@ -298,16 +339,16 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
   __syncthreads();
 }
 
-template <int NST>
+template <int NST, bool FP8>
 __global__ __launch_bounds__(256) void indexer_score_prefill_kernel(IndexerParams p) {
-  __shared__ __attribute__((aligned(16))) char ring[NST * kIdxTileBytes];
+  __shared__ __attribute__((aligned(16))) char ring[NST * (FP8 ? kIdxStageFp8 : kIdxTileBytes)];
   __shared__ int item_s;
   extern __shared__ int32_t pages_lds[];   // page ids of the tile's block range
   for (;;) {
     const int k = take_item(p.sched, &item_s);
     if (k < 0) break;
     const IdxTile T = idx_tile_of(p, p.worklist[k]);
-    indexer_prefill_tile<NST>(p, T, ring, pages_lds);
+    indexer_prefill_tile<NST, FP8>(p, T, ring, pages_lds);
   }
 }
 
@@ -318,17 +359,28 @@ hipError_t launch_indexer_prefill(const IndexerParams& p, int num_cus, hipStream
                      (size_t)(p.nbmax + 1) * sizeof(int), s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Two workgroups per CU with two-stage rings when both fit in 160 KiB of
-  // LDS (two waves per SIMD hide each other's LDS and MFMA latencies);
-  // otherwise one workgroup per CU with a deeper ring.
+  // Two workgroups per CU when their rings fit in 160 KiB of LDS (two waves
+  // per SIMD hide each other's LDS and MFMA latencies), the deeper ring
+  // first; otherwise one workgroup per CU with as deep a ring as fits.
   const size_t pages = (size_t)p.nbmax * sizeof(int32_t);
   const size_t lds_cu = 160 * 1024;
-  if (2 * (2 * kIdxTileBytes + pages + 64) <= lds_cu)
-    hipLaunchKernelGGL(indexer_score_prefill_kernel<2>, dim3(2 * num_cus), dim3(256), pages, s, p);
-  else if (4 * kIdxTileBytes + pages + 64 <= lds_cu)
-    hipLaunchKernelGGL(indexer_score_prefill_kernel<4>, dim3(num_cus), dim3(256), pages, s, p);
-  else
-    hipLaunchKernelGGL(indexer_score_prefill_kernel<3>, dim3(num_cus), dim3(256), pages, s, p);
+  const size_t stage = p.ik_fp8 ? kIdxStageFp8 : kIdxTileBytes;
+  auto fits = [&](int nst, int per_cu) { return per_cu * (nst * stage + pages + 64) <= lds_cu; };
+  const dim3 block(256);
+#define MSA_IDX_LAUNCH(NST, PER_CU)                                                                 \
+  do {                                                                                            \
+    if (p.ik_fp8)                                                                                 \
+      hipLaunchKernelGGL((indexer_score_prefill_kernel<NST, true>), dim3((PER_CU) * num_cus), block, \
+                         pages, s, p);                                                            \
+    else                                                                                          \
+      hipLaunchKernelGGL((indexer_score_prefill_kernel<NST, false>), dim3((PER_CU) * num_cus), block, \
+                         pages, s, p);                                                            \
+  } while (0)
+  if (fits(4, 2)) MSA_IDX_LAUNCH(4, 2);
+  else if (fits(2, 2)) MSA_IDX_LAUNCH(2, 2);
+  else if (fits(4, 1)) MSA_IDX_LAUNCH(4, 1);
+  else MSA_IDX_LAUNCH(3, 1);
+#undef MSA_IDX_LAUNCH
   return hipGetLastError();
 }
 

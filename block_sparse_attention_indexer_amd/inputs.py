@@ -9,7 +9,9 @@ Layout (all tensors are torch tensors on the requested device):
 
 * ``q``        bf16 ``[R, H_q, 128]``   attention queries, ragged rows
 * ``q_idx``    bf16 ``[R, H_kv, 128]``  indexer queries, one per KV head
-* ``index_k``  bf16 ``[P, H_ik, 128, 128]`` index-K page pool
+* ``index_k``  bf16 ``[P, H_ik, 128, 128]`` index-K page pool, or (FP8
+  index-K) float8_e4m3fn codes of that shape with ``index_k_scale`` float32
+  ``[P, H_ik, 128]``, both views of one buffer of 132 bytes per token
 * ``k_cache`` / ``v_cache`` bf16 or float8_e4m3fn ``[P, H_kv, 128, 128]``
 * ``input_row_offsets`` int32 ``[B+1]``, ``cache_lengths`` int32 ``[B]``,
   ``kv_lookup_table`` int32 ``[B, lookup_stride]``
@@ -57,6 +59,7 @@ class Workload:
     init_blocks: int
     local_blocks: int
     kv_dtype: str = "bf16"   # "bf16" or "fp8_e4m3"
+    ik_dtype: str = "bf16"   # index-K: "bf16" or "fp8_e4m3" (codes + per-token scale)
     kv_sigma: float = 1.0
     num_ik_heads: int = 1    # index-K heads stored in the cache: 1 or H_kv
     boost_frac: float = 0.0  # fraction of index-K rows multiplied by `boost`
@@ -160,12 +163,21 @@ def decode_fp8_long(seed: int = 0, batch: int = 16, ctx: int = 131072) -> Worklo
                     kv_dtype="fp8_e4m3", kv_sigma=0.5, seed=seed)
 
 
+def decode_fp8_long_fp8ik(seed: int = 0) -> Workload:
+    """The long-context FP8 decode with an FP8 index-K cache as well (e4m3
+    codes + one float32 scale per token, 132 bytes per token instead of 256):
+    batch 16, context 131072, 8 KV heads x GQA 8, top-k 64 (init 1, local 4)."""
+    wl = decode_fp8_long(seed)
+    return replace(wl, name="decode_fp8kv_fp8ik_b16_ctx128k_topk64", ik_dtype="fp8_e4m3")
+
+
 WORKLOADS = {
     "decode_small": decode_small,
     "decode_batch64": decode_batch64,
     "spec_decode": spec_decode,
     "prefill_ragged": prefill_ragged,
     "decode_fp8_long": decode_fp8_long,
+    "decode_fp8_long_fp8ik": decode_fp8_long_fp8ik,
 }
 
 
@@ -187,6 +199,7 @@ class Inputs:
     cache_lengths: torch.Tensor
     kv_lookup_table: torch.Tensor
     page_of: list = field(default_factory=list)   # host copy: page ids per sequence
+    index_k_scale: Optional[torch.Tensor] = None  # float32 [P, H_ik, 128] for FP8 index-K
 
     @property
     def device(self):
@@ -271,18 +284,43 @@ def make_inputs(wl: Workload, device="cpu") -> Inputs:
             rows = index_k[hp, :, hs, :].float() * wl.boost
             index_k[hp, :, hs, :] = rows.to(torch.bfloat16)
 
+    # FP8 index-K: the same values stored as e4m3 codes with one float32 scale
+    # per (page, head, slot), scale = max |value| / 448 over the slot's 128
+    # dims (1 for an all-zero slot), code = value / scale rounded to nearest
+    # even by torch's cast.  Page layout: each head's 128 x 128 code bytes
+    # followed by its 128 scales, i.e. 132 bytes per token.
+    index_k_scale = None
+    if wl.ik_dtype == "fp8_e4m3":
+        head_bytes = BLOCK * HEAD_DIM + BLOCK * 4
+        store = torch.empty((P, H_ik, head_bytes), dtype=torch.uint8, device=device)
+        codes = store[:, :, :BLOCK * HEAD_DIM].view(torch.float8_e4m3fn).unflatten(2, (BLOCK, HEAD_DIM))
+        index_k_scale = store[:, :, BLOCK * HEAD_DIM:].view(torch.float32)
+        for p0 in range(0, P, 1024):
+            vals = index_k[p0:p0 + 1024].float()
+            amax = vals.abs().amax(dim=-1)
+            sc = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+            codes[p0:p0 + 1024] = (vals / sc.unsqueeze(-1)).to(torch.float8_e4m3fn)
+            index_k_scale[p0:p0 + 1024] = sc
+        index_k = codes
+    elif wl.ik_dtype != "bf16":
+        raise ValueError(f"unsupported index-K dtype {wl.ik_dtype}")
+
     # Poison every slot that no sequence may read.
     nan = float("nan")
     unused = np.setdiff1d(np.arange(pool), np.concatenate(page_of) if page_of else [])
     poison_pages = torch.from_numpy(np.append(unused, trap).astype(np.int64)).to(device)
     for t in (index_k, k_cache, v_cache):
         t[poison_pages] = nan
+    if index_k_scale is not None:
+        index_k_scale[poison_pages] = nan
     for b in range(B):
         L = wl.seq_lens()[b]
         if L % BLOCK:
             last = int(page_of[b][-1])
             for t in (index_k, k_cache, v_cache):
                 t[last, :, L % BLOCK:, :] = nan
+            if index_k_scale is not None:
+                index_k_scale[last, :, L % BLOCK:] = nan
 
     offs = np.zeros(B + 1, dtype=np.int32)
     offs[1:] = np.cumsum(wl.new_lens)
@@ -291,7 +329,7 @@ def make_inputs(wl: Workload, device="cpu") -> Inputs:
         input_row_offsets=torch.from_numpy(offs).to(device),
         cache_lengths=torch.tensor(wl.cache_lens, dtype=torch.int32, device=device),
         kv_lookup_table=torch.from_numpy(table).to(device),
-        page_of=page_of,
+        page_of=page_of, index_k_scale=index_k_scale,
     )
 
 

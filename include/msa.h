@@ -81,11 +81,14 @@ enum msa_status {
     MSA_ERR_DEVICE = -7      /* no current HIP device, or it is not gfx950           */
 };
 
-/* Storage types of the paged caches ("msa" page: the index-K cache is always
- * BF16; the main K/V cache is BF16 or native FP8 e4m3 with no scales). */
+/* Storage types of the paged caches.  K/V ("msa" page): BF16 or native FP8
+ * e4m3 with no scales.  Index-K: BF16 ("msa" page), or FP8 e4m3 with one
+ * float32 dequantization scale per token ("DeepSeekSparseAttentionConfig"
+ * page, indexer_k_dtype field: 128 code bytes + a 4-byte scale per token at
+ * head dim 128), k_idx(j)[d] = e4m3(code[j][d]) * scale[j]. */
 enum msa_dtype {
     MSA_DTYPE_BF16 = 0,
-    MSA_DTYPE_FP8_E4M3 = 1   /* OCP e4m3fn: bias 7, max 448, no inf, value x 1.0 */
+    MSA_DTYPE_FP8_E4M3 = 1   /* OCP e4m3fn: bias 7, max 448, no inf          */
 };
 
 enum {
@@ -110,6 +113,15 @@ typedef struct msa_paged_cache {
     int64_t token_stride;    /* elements between slots of one head; >= 128, and   */
                              /* the 128 slots of a page span < 2 GiB              */
                              /* (token_stride * element size * 128 <= INT32_MAX)  */
+    /* Per-token dequantization scales: FP8 index-K caches only (NULL for
+     * BF16 caches and for K/V).  The scale of slot t of head h of page p is
+     * scale[p*scale_page_stride + h*scale_head_stride + t]; the 128 slots of
+     * a head are contiguous.  16-byte aligned, strides multiples of 4.  The
+     * scales may sit inside the code pages (e.g. each head's 128 x 128 codes
+     * followed by its 128 scales: 132 bytes per token). */
+    const float* scale;
+    int64_t scale_page_stride;  /* floats between pages                          */
+    int64_t scale_head_stride;  /* floats between heads of one page              */
 } msa_paged_cache;
 
 /* The ragged batch: which rows are whose, and where their KV lives. */
@@ -148,14 +160,17 @@ size_t msa_indexer_workspace_bytes(const msa_ragged* rg, int32_t num_kv_heads,
  *   Otherwise every block outside F is scored with
  *     s(blk) = max over j in blk, j <= p of  sum_d q_idx[r][h][d] * k_idx(j)[d]
  *   (FP32 accumulation, no softmax scale), where k_idx(j) is head
- *   h % index_k->num_heads of position j in the index-K cache, and the
+ *   h % index_k->num_heads of position j in the index-K cache (for an FP8
+ *   cache, e4m3(code) * scale of that slot: the dot product of q_idx with
+ *   the codes, then times the scale), and the
  *   top_k - |F| highest scores join F; equal scores go to the lower id.
  *   d_indices[r][h][:] = the selection in ascending order, padded with -1.
  *
  * d_indices     device int32 [batch*max_seq_length rows max][num_kv_heads][top_k];
  *               rows >= input_row_offsets[batch] are not written.
  * q_idx         device bf16 [rows][num_kv_heads][128].
- * index_k       BF16 cache with num_heads 1 (shared by all KV heads) or
+ * index_k       BF16 cache, or FP8 e4m3 cache with per-token scales (scale
+ *               non-NULL), with num_heads 1 (shared by all KV heads) or
  *               num_kv_heads.
  * top_k         1 .. MSA_MAX_TOPK; init_blocks, local_blocks >= 0 with
  *               init_blocks + local_blocks <= top_k.
@@ -205,7 +220,7 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
  * q             device bf16 [rows][num_q_heads][128].
  * d_indices     device int32 [rows][num_kv_heads][top_k] (the indexer's output).
  * k_cache, v_cache  caches with num_heads == num_kv_heads and the same dtype
- *               (BF16 or FP8 e4m3).
+ *               (BF16 or FP8 e4m3, scale-free: scale must be NULL).
  * num_q_heads   a multiple of num_kv_heads with group size 1, 2, 4, 8 or 16.
  * scale         softmax scale applied to q.k (e.g. 1/sqrt(128)); positive
  *               and finite.

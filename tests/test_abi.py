@@ -5,6 +5,7 @@ import ctypes
 import re
 
 import pytest
+import torch
 
 from block_sparse_attention_indexer_amd import binding as B
 
@@ -59,7 +60,7 @@ def test_indexer_validation():
     assert indexer(rg(), cache(tok=100)) == SHAPE            # unaligned stride
     assert indexer(rg(), cache(data=FAKE + 2)) == SHAPE      # unaligned base
     assert indexer(rg(), cache(tok=1 << 23)) == SHAPE        # a page's rows span >= 2 GiB
-    assert indexer(rg(), cache(dtype=B.MSA_DTYPE_FP8_E4M3)) == DTYPE
+    assert indexer(rg(), cache(dtype=B.MSA_DTYPE_FP8_E4M3)) == NULL   # FP8 without its scales
     assert indexer(rg(), cache(dtype=7)) == DTYPE
     assert indexer(rg(), cache(), top_k=0) == PARAM
     assert indexer(rg(), cache(), top_k=2, init=2, local=1) == PARAM
@@ -71,6 +72,37 @@ def test_indexer_validation():
     assert need >= 2 * 8 * 32 * 4
     assert indexer(rg(), cache(), ws=need - 1) == WORKSPACE
     assert B.msa_indexer_workspace_bytes(rg(max_cache=1000), 8, 16) == 0   # nb <= top_k
+
+
+def test_index_k_scale_rules():
+    # FP8 index-K needs its per-token scales; BF16 index-K and K/V take none
+    c8 = cache(dtype=B.MSA_DTYPE_FP8_E4M3)
+    assert indexer(rg(), c8) == NULL                                  # scales missing
+    c8.scale, c8.scale_page_stride, c8.scale_head_stride = FAKE, 4224, 4224
+    assert indexer(rg(), c8) == NULL                                  # passes to the workspace check
+    c8.scale = FAKE + 4
+    assert indexer(rg(), c8) == SHAPE                                 # unaligned scales
+    c8.scale, c8.scale_head_stride = FAKE, 4222
+    assert indexer(rg(), c8) == SHAPE                                 # stride not a multiple of 4
+    c16 = cache()
+    c16.scale = FAKE
+    assert indexer(rg(), c16) == DTYPE                                # BF16 index-K with scales
+    k, v = cache(heads=8), cache(heads=8)
+    k.scale = FAKE
+    assert attention(rg(), k, v) == DTYPE                             # K/V are scale-free
+
+
+def test_binding_describes_the_fp8_index_k_page_layout():
+    # 128 x 128 codes then 128 float32 scales per (page, head): 132 B per token
+    P, H = 3, 2
+    store = torch.zeros((P, H, 128 * 128 + 128 * 4), dtype=torch.uint8)
+    codes = store[:, :, :128 * 128].view(torch.float8_e4m3fn).unflatten(2, (128, 128))
+    scales = store[:, :, 128 * 128:].view(torch.float32)
+    c = B.paged_cache(codes, scales)
+    assert c.dtype == B.MSA_DTYPE_FP8_E4M3
+    assert (c.page_stride, c.head_stride, c.token_stride) == (H * 16896, 16896, 128)
+    assert (c.scale_page_stride, c.scale_head_stride) == (H * 4224, 4224)
+    assert c.scale - c.data == 128 * 128
 
 
 def test_attention_validation():

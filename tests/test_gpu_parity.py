@@ -50,11 +50,11 @@ def run_and_check(wl, seqs=None, per_seq=None, num_partitions=0):
 
 
 def wl_custom(name, new, cached, H_kv=2, G=8, top_k=6, init=1, local=2, kv="bf16", H_ik=1,
-              boost=0.0, seed=3):
+              boost=0.0, seed=3, ik="bf16"):
     return I.Workload(name, new_lens=tuple(new), cache_lens=tuple(cached), num_kv_heads=H_kv,
                       group=G, top_k=top_k, init_blocks=init, local_blocks=local, kv_dtype=kv,
                       kv_sigma=0.5 if kv != "bf16" else 1.0, num_ik_heads=H_ik, boost_frac=boost,
-                      seed=seed)
+                      seed=seed, ik_dtype=ik)
 
 
 # --- the five workloads ------------------------------------------------------
@@ -242,3 +242,24 @@ def test_prefill_tile_edges():
     # lengths around the 32-token tile and the 128-token block
     run_and_check(wl_custom("prefill_edges", [9, 31, 32, 33, 129], [127, 128, 0, 4000, 255],
                             top_k=4), per_seq=None)
+
+
+# --- FP8 index-K (e4m3 codes + one float32 scale per token) ---------------
+
+def test_fp8_index_k_decode_and_spec():
+    run_and_check(wl_custom("ik8_decode", [1, 1, 1], [5000, 300, 9000], ik="fp8_e4m3", boost=0.05))
+    run_and_check(wl_custom("ik8_spec", [3, 8, 1, 5], [3000, 2500, 700, 4000], top_k=8,
+                            ik="fp8_e4m3"))
+    run_and_check(wl_custom("ik8_heads", [1, 4], [4000, 2600], H_kv=4, H_ik=4, init=0, local=0,
+                            top_k=3, ik="fp8_e4m3"))
+
+
+def test_fp8_index_k_prefill():
+    run_and_check(wl_custom("ik8_prefill", [200, 45, 300], [1000, 5000, 0], top_k=5,
+                            ik="fp8_e4m3"), per_seq=30)
+    run_and_check(wl_custom("ik8_prefill_heads", [130, 40], [3000, 9000], H_kv=2, H_ik=2, G=4,
+                            top_k=6, ik="fp8_e4m3"), per_seq=30)
+
+
+def test_fp8_index_k_long_context_full_sampled():
+    run_and_check(I.decode_fp8_long_fp8ik(), seqs=[0, 7, 15])
