@@ -338,19 +338,20 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   uint32_t key[KPL];
 #pragma unroll
   for (int s = 0; s < KPL; ++s) key[s] = s * 64 + lane < ncand ? score_key(v[s]) : 0u;
+  // Keys of slots past the candidates are 0, below every candidate key and
+  // below every trial value, so the counts need no per-slot guard (a
+  // branch-free compare / ballot / popcount stream per bit).
   uint32_t thr = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int s = 0; s < KPL; ++s)
-      if (s < nslot) cnt += __popcll(ballot(key[s] >= cand));
+    for (int s = 0; s < KPL; ++s) cnt += __popcll(ballot(key[s] >= cand));
     if (cnt >= kfree) thr = cand;
   }
   int above = 0;
 #pragma unroll
-  for (int s = 0; s < KPL; ++s)
-    if (s < nslot) above += __popcll(ballot(key[s] > thr));
+  for (int s = 0; s < KPL; ++s) above += __popcll(ballot(key[s] > thr));
   const int need_eq = kfree - above;
   int run = 0, run_eq = 0;
 #pragma unroll
