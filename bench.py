@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch64",
                     help="decode_small | decode_batch64 | spec_decode | prefill_ragged | "
-                         "decode_fp8_long | decode_fp8_long_fp8ik | all")
+                         "decode_fp8_long | decode_fp8_long_fp8ik | spec_decode_reuse | all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
@@ -302,7 +302,11 @@ def run(workload, args):
     from block_sparse_attention_indexer_amd import binding as B
     from block_sparse_attention_indexer_amd import inputs as I
 
-    wl = I.WORKLOADS[workload]()
+    # "<workload>_reuse": a draft step that reuses an earlier step's block
+    # selection (each row takes its sequence's first row's ids) instead of
+    # running the indexer
+    reuse = workload.endswith("_reuse")
+    wl = I.WORKLOADS[workload[:-len("_reuse")] if reuse else workload]()
     prefill = wl.max_seq_length > 8
     inp = I.make_inputs(wl, "cuda")
     rg = B.ragged_of_inputs(inp)
@@ -320,6 +324,16 @@ def run(workload, args):
         B.msa_indexer_paged(d, inp.q_idx, inp.index_k, rg, wl.num_kv_heads, wl.top_k,
                             wl.init_blocks, wl.local_blocks, ws_i, stream,
                             index_k_scale=inp.index_k_scale)
+
+    if reuse:
+        indexer()
+        d_prev = d.clone()
+        offs = inp.input_row_offsets.cpu().numpy()
+        src = torch.from_numpy(np.concatenate(
+            [np.full(offs[b + 1] - offs[b], offs[b]) for b in range(wl.batch)]).astype(np.int32)).cuda()
+
+        def indexer():      # noqa: F811 - the draft step's selection
+            B.msa_indexer_reuse(d, d_prev, src, stream)
 
     def attention():
         B.msa_attention_paged(out, inp.q, d, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
@@ -377,6 +391,9 @@ def run(workload, args):
     attn_kernel_ms = max(att_ms - comb_ms, 1e-6)
 
     work = algorithmic_work(wl, d.cpu().numpy())
+    if reuse:
+        # the reused selection reads no index-K and scores nothing
+        work["ik_bytes"] = work["idx_flops"] = 0
     ms = wall / K * 1e3
     tok_s = wl.total_rows / (wall / K)
     # The roofline's duration is one attention call: the attention kernel
@@ -406,7 +423,9 @@ def run(workload, args):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.kv_dtype == "bf16" else "fp8_e4m3 kv / bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.total_rows,
+        "config": {"workload": wl.name + (" draft step, top-k reused from each sequence's first "
+                                          "draft token" if reuse else ""),
+                   "batch": wl.batch, "new_tokens": wl.total_rows,
                    "max_context": max(wl.seq_lens()), "kv_heads": wl.num_kv_heads,
                    "gqa": wl.group, "top_k": wl.top_k, "init_blocks": wl.init_blocks,
                    "local_blocks": wl.local_blocks, "kv_dtype": wl.kv_dtype,
@@ -441,7 +460,7 @@ def main():
         write_traffic_record(args)
         return
     names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long",
-              "decode_fp8_long_fp8ik"]
+              "decode_fp8_long_fp8ik", "spec_decode_reuse"]
              if args.workload == "all" else [args.workload])
     for name in names:
         print(json.dumps(run(name, args)), flush=True)

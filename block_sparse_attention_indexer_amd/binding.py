@@ -72,6 +72,9 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged),
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "msa_indexer_reuse": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "msa_attention_partitions": (ctypes.c_int, [
         ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "msa_attention_workspace_bytes": (ctypes.c_size_t, [
@@ -206,6 +209,22 @@ def msa_indexer_paged(d_indices, q_idx, index_k, rg: Ragged, num_kv_heads: int, 
                                      local_blocks, _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream))
     _check(st, "msa_indexer_paged")
+    return d_indices
+
+
+def msa_indexer_reuse(d_indices, prev_indices, src_row, stream=None):
+    """d_indices[r] = prev_indices[src_row[r]] (all KV heads); rows whose source
+    is out of range get -1.  int32 tensors [rows, H_kv, top_k],
+    [prev_rows, H_kv, top_k] and [rows]."""
+    rows, H_kv, top_k = d_indices.shape
+    if prev_indices.shape[1:] != (H_kv, top_k) or src_row.shape != (rows,):
+        raise ValueError("shapes of d_indices, prev_indices and src_row do not match")
+    for t in (d_indices, prev_indices, src_row):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("block ids and source rows must be contiguous int32")
+    st = library().msa_indexer_reuse(_ptr(d_indices), _ptr(prev_indices), _ptr(src_row), rows,
+                                     prev_indices.shape[0], H_kv, top_k, _stream(stream))
+    _check(st, "msa_indexer_reuse")
     return d_indices
 
 

@@ -294,6 +294,24 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   return MSA_OK;
 }
 
+int msa_indexer_reuse(int32_t* d_indices, const int32_t* prev_indices, const int32_t* src_row,
+                      int32_t rows, int32_t prev_rows, int32_t num_kv_heads, int32_t top_k,
+                      void* stream) {
+  if (rows < 0 || prev_rows < 0 || num_kv_heads < 1) return MSA_ERR_PARAM;
+  if (top_k < 1 || top_k > MSA_MAX_TOPK) return MSA_ERR_PARAM;
+  if (rows == 0) return MSA_OK;
+  if (!d_indices || !prev_indices || !src_row) return MSA_ERR_NULL;
+  if ((int64_t)rows * num_kv_heads * top_k > (int64_t)INT32_MAX ||
+      (int64_t)prev_rows * num_kv_heads * top_k > (int64_t)INT32_MAX)
+    return MSA_ERR_SHAPE;
+  const int st = current_device(nullptr);
+  if (st != MSA_OK) return st;
+  if (launch_indexer_reuse(d_indices, prev_indices, src_row, rows, prev_rows,
+                           num_kv_heads * top_k, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MSA_ERR_LAUNCH;
+  return MSA_OK;
+}
+
 int msa_attention_partitions(const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t top_k, int32_t num_partitions) {
   int st = check_ragged(rg);

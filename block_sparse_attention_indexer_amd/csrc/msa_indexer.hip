@@ -368,6 +368,29 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Selection reuse across draft steps: a row gather.  One workgroup per 8
+// rows (one wave per two rows' worth of ids at width 8 x 64); the source
+// row is read once per row and broadcast.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reuse_kernel(int32_t* out, const int32_t* prev, const int32_t* src,
+                                                    int rows, int prev_rows, int width) {
+  const int r = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (r >= rows) return;
+  const int sr = src[r];
+  const bool ok = sr >= 0 && sr < prev_rows;
+  int32_t* o = out + (size_t)r * width;
+  const int32_t* in = prev + (size_t)(ok ? sr : 0) * width;
+  for (int i = threadIdx.x & 31; i < width; i += 32) o[i] = ok ? in[i] : -1;
+}
+
+hipError_t launch_indexer_reuse(int32_t* out, const int32_t* prev, const int32_t* src, int rows,
+                                int prev_rows, int width, hipStream_t s) {
+  hipLaunchKernelGGL(reuse_kernel, dim3((rows + 7) / 8), dim3(256), 0, s, out, prev, src, rows,
+                     prev_rows, width);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s) {
   const int ncand_max = p.nbmax - p.init - p.local;
   dim3 grid((p.rg.max_seq * p.H_kv + 3) / 4, p.rg.batch);

@@ -80,6 +80,10 @@ struct CombineParams {
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_t s);
+// out[r][:] = prev[src[r]][:] (row length `width` ints), -1 rows for sources
+// outside [0, prev_rows)
+hipError_t launch_indexer_reuse(int32_t* out, const int32_t* prev, const int32_t* src, int rows,
+                                int prev_rows, int width, hipStream_t s);
 hipError_t launch_indexer_prefill(const IndexerParams& p, int num_cus, hipStream_t s);
 int prefill_indexer_tile(int H_kv, int H_ik);
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s);

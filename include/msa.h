@@ -185,6 +185,30 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx,
                       int32_t local_blocks, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * Reuse of a previous step's block selection across draft steps
+ * ("DeepSeekSparseAttentionConfig" page, index_share_for_mtp_iteration
+ * field: reuse the indexer top-k across MTP draft steps instead of
+ * recomputing it).  The rows of a draft step take the selection of a row of
+ * an earlier step unchanged, for every KV head:
+ *   d_indices[r][h][:] = prev_indices[src_row[r]][h][:]   for r < rows;
+ * a row whose src_row[r] is outside [0, prev_rows) gets -1 everywhere (no
+ * block).  The attention then applies each row's own causal clip (j <= p)
+ * to the reused blocks; blocks a later position could see but the source
+ * row did not select are not attended.
+ *
+ * d_indices     device int32 [rows][num_kv_heads][top_k], written.
+ * prev_indices  device int32 [prev_rows][num_kv_heads][top_k]; may not
+ *               overlap d_indices.
+ * src_row       device int32 [rows].
+ *
+ * Errors: MSA_ERR_NULL, MSA_ERR_PARAM, MSA_ERR_SHAPE, MSA_ERR_LAUNCH.  rows
+ * == 0 is a no-op.
+ */
+int msa_indexer_reuse(int32_t* d_indices, const int32_t* prev_indices, const int32_t* src_row,
+                      int32_t rows, int32_t prev_rows, int32_t num_kv_heads, int32_t top_k,
+                      void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sparse attention                                                         */
 /* ------------------------------------------------------------------------ */

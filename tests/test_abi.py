@@ -105,6 +105,18 @@ def test_binding_describes_the_fp8_index_k_page_layout():
     assert c.scale - c.data == 128 * 128
 
 
+def test_reuse_validation():
+    lib = B.library()
+    assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, 0, 0, 8, 16, None) == OK       # no rows
+    assert lib.msa_indexer_reuse(None, FAKE, FAKE, 4, 2, 8, 16, None) == NULL
+    assert lib.msa_indexer_reuse(FAKE, FAKE, None, 4, 2, 8, 16, None) == NULL
+    assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, -1, 2, 8, 16, None) == PARAM
+    assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, 4, 2, 0, 16, None) == PARAM
+    assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, 4, 2, 8, 0, None) == PARAM
+    assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, 4, 2, 8, 513, None) == PARAM
+    assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, 1 << 20, 2, 64, 512, None) == SHAPE
+
+
 def test_attention_validation():
     k = cache(heads=8)
     v = cache(heads=8)

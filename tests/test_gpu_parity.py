@@ -263,3 +263,32 @@ def test_fp8_index_k_prefill():
 
 def test_fp8_index_k_long_context_full_sampled():
     run_and_check(I.decode_fp8_long_fp8ik(), seqs=[0, 7, 15])
+
+
+# --- selection reuse across draft steps ---------------------------------------
+
+def test_reuse_gathers_rows_and_feeds_attention():
+    # every draft token reuses its sequence's first token's selection; two
+    # extra rows name out-of-range sources and must come back empty
+    wl = wl_custom("reuse", [3, 8, 1, 5], [6000, 2500, 700, 4000], top_k=8)
+    inp = I.make_inputs(wl, DEV)
+    d_prev = B.run_indexer(inp)
+    offs = inp.input_row_offsets.cpu().numpy()
+    src = np.concatenate([np.full(offs[b + 1] - offs[b], offs[b]) for b in range(wl.batch)])
+    src_t = torch.from_numpy(src.astype(np.int32)).to(DEV)
+    d = torch.empty_like(d_prev)
+    B.msa_indexer_reuse(d, d_prev, src_t)
+    torch.cuda.synchronize()
+    assert torch.equal(d, d_prev[src_t.long()])
+    bad = torch.tensor([-1, d_prev.shape[0]], dtype=torch.int32, device=DEV)
+    d_bad = torch.empty((2,) + tuple(d_prev.shape[1:]), dtype=torch.int32, device=DEV)
+    B.msa_indexer_reuse(d_bad, d_prev, bad)
+    torch.cuda.synchronize()
+    assert (d_bad == -1).all()
+    # attention on the reused selections, each row with its own causal clip
+    out = B.run_attention(inp, d)
+    torch.cuda.synchronize()
+    pb, orig = O.problem_for_sequences(inp, list(range(wl.batch)))
+    rows = list(range(len(orig)))
+    ref = O.attention(pb, d.cpu().numpy()[orig], rows)
+    parity.check_attention(out[torch.as_tensor(orig, device=DEV)], ref, wl.kv_dtype, "reuse")
