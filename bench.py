@@ -19,11 +19,18 @@ synchronize and two HIP events on the launch stream, with nothing else
 enqueued between them; value and ms_per_step come from the host wall clock
 over those K steps.
 
-Roofline: the dominant kernel is the sparse-attention kernel.  Its average
-duration is measured live with HIP events on the launch stream: K
-back-to-back attention calls between two events, minus K back-to-back split-K
-combines of the same shape when the call enqueues one; achieved =
-algorithmic bytes (or flops) of one launch / that duration.
+Roofline: the dominant kernel is the sparse-attention kernel.  Its duration
+is one attention call as the library enqueues it (the kernel, plus the
+split-K combine when the row is split), measured live with HIP events on the
+launch stream over K back-to-back calls; achieved = algorithmic bytes (or
+flops) of one call / that duration.
+
+Latent workload (--workload latent_decode): one step is one
+msa_latent_attention_paged call; the metric is the latent bytes it must
+gather (window positions and valid listed entries, 256 bytes each) per
+second.  The steps rotate over input sets of the same shape with different
+data, so that the data of consecutive steps does not stay in the GPU's
+last-level cache.
 
 CPU baseline: the oracle (plain NumPy, as written -- not tuned) timed on the
 host cores on a bounded sample of the same workload's rows.
@@ -54,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch64",
                     help="decode_small | decode_batch64 | spec_decode | prefill_ragged | "
-                         "decode_fp8_long | decode_fp8_long_fp8ik | spec_decode_reuse | all")
+                         "decode_fp8_long | decode_fp8_long_fp8ik | spec_decode_reuse | "
+                         "latent_decode | all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
@@ -108,6 +116,27 @@ def algorithmic_work(wl, d_idx, rows=None):
             k = np.where(nb > wl.top_k, nb - wl.local_blocks - wl.init_blocks, 0)
             idx_flops += 2 * 128 * wl.num_kv_heads * 128 * int(k.sum())
     return dict(kv_bytes=kv_bytes, ik_bytes=ik_bytes, attn_flops=attn_flops, idx_flops=idx_flops)
+
+
+def latent_work(inp):
+    """Latent bytes one call must gather: for every row and latent head, its
+    window positions plus its listed entries inside the compressed leaf (each
+    occurrence), 256 bytes each (one BF16 vector of 128); and flops, 4 * 128
+    per (query head, entry)."""
+    wl = inp.wl
+    offs = inp.input_row_offsets.cpu().numpy()
+    swa_c = inp.swa_cache_lengths.cpu().numpy()
+    comp_c = inp.comp_cache_lengths.cpu().numpy()
+    lists = inp.comp_indices.cpu().numpy()
+    ent = 0
+    for b in range(wl.batch):
+        for r in range(offs[b], offs[b + 1]):
+            p = int(swa_c[b]) + (r - offs[b])
+            n_swa = min(wl.window, p + 1) if wl.window > 0 else 0
+            lst = lists[r]
+            ent += wl.num_latent_heads * n_swa + int(((lst >= 0) & (lst < comp_c[b])).sum())
+    return {"entries": ent, "latent_bytes": ent * 256,
+            "flops": ent * 4 * 128 * (wl.num_heads // wl.num_latent_heads)}
 
 
 # ---------------------------------------------------------------------------
@@ -187,9 +216,19 @@ def cpu_baseline(inp, wl, prefill, seconds):
 # the measured step
 # ---------------------------------------------------------------------------
 
-def kernel_source_hash():
+def is_latent(workload):
+    return workload.startswith("latent")
+
+
+def kernel_of(workload):
+    return "latent_attn_kernel" if is_latent(workload) else "attn_decode_kernel"
+
+
+def kernel_source_hash(workload="decode_batch64"):
     h = hashlib.sha256()
-    for f in ("msa_attention.hip", "msa_common.h", "msa_kernels.h"):
+    files = (("msa_latent.hip", "msa_lds.h", "msa_attention.hip", "msa_common.h", "msa_kernels.h")
+             if is_latent(workload) else ("msa_attention.hip", "msa_common.h", "msa_kernels.h"))
+    for f in files:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -197,11 +236,11 @@ def kernel_source_hash():
 def traffic_record(workload):
     """HBM traffic per launch of the attention kernel from committed rocprofv3
     counter runs, if they were taken on the current kernel source."""
-    path = os.path.join(PROFILES, f"attn_decode_kernel_{workload}_traffic.json")
+    path = os.path.join(PROFILES, f"{kernel_of(workload)}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -240,30 +279,37 @@ def write_traffic_record(args):
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         per = _counter_per_dispatch(path, counter)
         copy = max(v for name, vals in per.items() if "copy" in name.lower() for v in vals)
-        attn = [v for name, vals in per.items() if "attn_decode_kernel" in name for v in vals]
+        attn = [v for name, vals in per.items() if kernel_of(args.workload) in name for v in vals]
         comb = [v for name, vals in per.items() if "combine_kernel" in name for v in vals]
         if not attn:
-            raise SystemExit(f"no attn_decode_kernel dispatch in {path}")
+            raise SystemExit(f"no {kernel_of(args.workload)} dispatch in {path}")
         scale = COPY_BYTES / (copy * 1024.0)
         # one attention call: the attention kernel, plus the combine when split
         per_call = float(np.mean(attn)) + (float(np.mean(comb)) if comb else 0.0)
         raw[counter] = (per_call, copy, scale, len(attn), float(np.mean(comb)) if comb else 0.0)
         scaled[counter] = per_call * 1024.0 * scale
 
-    wl = I.WORKLOADS[args.workload]()
-    inp = I.make_inputs(wl, "cuda")
-    d = B.run_indexer(inp)
-    torch.cuda.synchronize()
-    algo = algorithmic_work(wl, d.cpu().numpy())["kv_bytes"]
+    if is_latent(args.workload):
+        from block_sparse_attention_indexer_amd import latent_inputs as LI
+        lw = LI.LATENT_WORKLOADS[args.workload]()
+        algo = latent_work(LI.make_latent_inputs(lw, "cpu"))["latent_bytes"]
+        wl_name = lw.name
+    else:
+        wl = I.WORKLOADS[args.workload]()
+        inp = I.make_inputs(wl, "cuda")
+        d = B.run_indexer(inp)
+        torch.cuda.synchronize()
+        algo = algorithmic_work(wl, d.cpu().numpy())["kv_bytes"]
+        wl_name = wl.name
     hbm = scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"]
     cmd = ("rocprofv3 --pmc {c} --kernel-include-regex "
-           "'attn_decode_kernel|combine_kernel|copy|elementwise' "
+           f"'{kernel_of(args.workload)}|combine_kernel|copy|elementwise' "
            "--output-format csv -d $R/gpurun_out/pmc_{w}_{l} -o run -- python3 $R/bench.py "
            "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration")
     rec = {
-        "kernel": ("msa::attn_decode_kernel" if not raw["FETCH_SIZE"][4] else
-                   "one attention call: msa::attn_decode_kernel + msa::combine_kernel"),
-        "workload": f"{args.workload} ({wl.name})",
+        "kernel": (f"msa::{kernel_of(args.workload)}" if not raw["FETCH_SIZE"][4] else
+                   f"one attention call: msa::{kernel_of(args.workload)} + msa::combine_kernel"),
+        "workload": f"{args.workload} ({wl_name})",
         "fetch_size_kib_per_launch": raw["FETCH_SIZE"][0],
         "write_size_kib_per_launch": raw["WRITE_SIZE"][0],
         "combine_fetch_write_kib_per_launch": [raw["FETCH_SIZE"][4], raw["WRITE_SIZE"][4]],
@@ -277,7 +323,7 @@ def write_traffic_record(args):
         "hbm_bytes_per_launch": int(round(hbm)),
         "algorithmic_gathered_kv_bytes_per_launch": int(algo),
         "hbm_over_algorithmic": hbm / algo if algo else None,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(args.workload),
         "commands": [cmd.format(c="FETCH_SIZE", w=args.workload, l="fetch"),
                      cmd.format(c="WRITE_SIZE", w=args.workload, l="write"),
                      f"python3 $R/bench.py --workload {args.workload} --traffic-record "
@@ -444,6 +490,124 @@ def run(workload, args):
     return res
 
 
+def run_latent(workload, args):
+    import torch
+    from dataclasses import replace
+
+    from block_sparse_attention_indexer_amd import binding as B
+    from block_sparse_attention_indexer_amd import latent_inputs as LI
+
+    wl = LI.LATENT_WORKLOADS[workload]()
+    first = LI.make_latent_inputs(wl, "cuda")
+    work = latent_work(first)
+    # enough input sets of the same shape (different data and lists) that the
+    # data the rotating steps read spans more than twice the 256 MB last-level
+    # cache
+    nsets = max(1, -(-2 * 256 * 2**20 // work["latent_bytes"]))
+    sets = [first] + [LI.make_latent_inputs(replace(wl, seed=wl.seed + 1000 + k), "cuda")
+                      for k in range(1, nsets)]
+    stream = torch.cuda.current_stream()
+    np_ = B.msa_latent_partitions(wl.batch, wl.max_seq_length, wl.num_heads, wl.num_latent_heads,
+                                  wl.window, wl.top_c, args.partitions)
+    ws = torch.empty(max(1, B.msa_latent_workspace_bytes(wl.batch, wl.max_seq_length, wl.num_heads,
+                                                         wl.num_latent_heads, wl.window, wl.top_c,
+                                                         np_)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.total_rows, wl.num_heads, 128), dtype=torch.bfloat16, device="cuda")
+    leaves = [B.latent_leaves_of_inputs(inp) for inp in sets]
+
+    def step(k):
+        inp = sets[k % nsets]
+        swa, comp = leaves[k % nsets]
+        B.msa_latent_attention_paged(out, inp.q, inp.input_row_offsets, wl.batch,
+                                     wl.max_seq_length, inp.comp_indices, inp.attn_sink, swa, comp,
+                                     wl.num_heads, wl.num_latent_heads, wl.window, wl.softmax_scale,
+                                     np_, ws, stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    K = args.steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(K):
+        step(k)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = t_start.elapsed_time(t_end) / K
+    ms = wall / K * 1e3
+    value = work["latent_bytes"] / (wall / K) / 1e9
+    # the roofline's duration: one call as the library enqueues it (kernel +
+    # split-K combine), from the events around the timed steps
+    achieved = work["latent_bytes"] / (gpu_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode gathered-KV GB/s (% HBM peak) + query tok/s; prefill TFLOP/s (% MFMA)",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + " (latent sparse attention: shared K=V latent, window "
+                                         "leaf + compressed leaf by per-token entry list, "
+                                         "per-head sink)",
+                   "batch": wl.batch, "new_tokens": wl.total_rows, "query_heads": wl.num_heads,
+                   "latent_heads": wl.num_latent_heads, "head_dim": 128, "window": wl.window,
+                   "top_c": wl.top_c, "context": [min(wl.swa_cache_lens) + 1, max(wl.swa_cache_lens) + 1],
+                   "compressed_leaf_entries": [min(wl.comp_lens), max(wl.comp_lens)],
+                   "leaf_dtype": wl.swa_dtype, "split_k_partitions": np_,
+                   "input_sets_rotated": nsets},
+        "query_tok_s": wl.total_rows / (wall / K),
+        "gpu_ms_per_step": gpu_ms,
+        "algorithmic": work,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload),
+                     "kernel": "latent call: latent_attn_kernel" +
+                               (" + combine_kernel (split-K)" if np_ > 1 else "")},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = latent_cpu_baseline(first, args.cpu_seconds)
+    return res
+
+
+def latent_cpu_baseline(inp, seconds):
+    """The latent oracle, as written, on the host cores: every sequence's rows
+    once, then further passes over them while the time budget lasts (only the
+    oracle's attention is timed, not the host copies of its inputs)."""
+    from oracle import latent_oracle as LO
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:  # pragma: no cover - reporting only
+        threads = 1
+    wl = inp.wl
+    offs = inp.input_row_offsets.cpu().numpy()
+    probs = []
+    for b in range(wl.batch):
+        pb, orig = LO.problem_for_sequences(inp, [b], list(range(offs[b], offs[b + 1])))
+        nb = 0
+        for r in range(len(orig)):
+            bb, _, p = LO.row_position(pb, r)
+            nb += 256 * sum(len(LO.window_positions(p, pb.window)) + len(LO.listed_entries(pb, r, hl, bb))
+                            for hl in range(pb.num_latent_heads))
+        probs.append((pb, len(orig), nb))
+    spent, nbytes, rows, passes = 0.0, 0, 0, 0
+    while spent < seconds:
+        for pb, n, nb in probs:
+            t0 = time.perf_counter()
+            LO.latent_attention(pb, range(n))
+            spent += time.perf_counter() - t0
+            nbytes += nb
+            rows += n
+        passes += 1
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} passes over all {wl.batch} sequences' rows ({rows} row evaluations, "
+                      f"{spent:.1f} s of oracle time)",
+            "query_tok_s": rows / spent,
+            "affinity_cpus": len(os.sched_getaffinity(0)), "os_cpus": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -460,10 +624,11 @@ def main():
         write_traffic_record(args)
         return
     names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long",
-              "decode_fp8_long_fp8ik", "spec_decode_reuse"]
+              "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode"]
              if args.workload == "all" else [args.workload])
     for name in names:
-        print(json.dumps(run(name, args)), flush=True)
+        res = run_latent(name, args) if is_latent(name) else run(name, args)
+        print(json.dumps(res), flush=True)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
         dst = torch.empty_like(src)

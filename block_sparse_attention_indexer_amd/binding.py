@@ -63,6 +63,19 @@ class Ragged(ctypes.Structure):
     ]
 
 
+class LatentLeaf(ctypes.Structure):
+    _fields_ = [
+        ("cache", PagedCache),
+        ("cache_lengths", ctypes.c_void_p),
+        ("lookup_table", ctypes.c_void_p),
+        ("lookup_stride", ctypes.c_int32),
+        ("max_cache_length", ctypes.c_int32),
+    ]
+
+
+MSA_LATENT_MAX_TOPC = 16384
+MSA_LATENT_MAX_WINDOW = 1 << 20
+
 _lib = None
 
 _SIGNATURES = {
@@ -84,6 +97,13 @@ _SIGNATURES = {
         ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p]),
+    "msa_latent_partitions": (ctypes.c_int, [ctypes.c_int32] * 7),
+    "msa_latent_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 7),
+    "msa_latent_attention_paged": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(LatentLeaf),
+        ctypes.POINTER(LatentLeaf), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "msa_splitk_combine": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
@@ -253,6 +273,57 @@ def msa_splitk_combine(output, partial_o, partial_lse, input_row_offsets, batch:
     return output
 
 
+def latent_leaf(pool: torch.Tensor, cache_lengths, lookup_table, max_cache_length: int) -> LatentLeaf:
+    """Describe one leaf of the latent cache: pool [pages, latent heads, 128,
+    128], cache lengths [batch] and page lookup table [batch, stride] (int32)."""
+    for t in (cache_lengths, lookup_table):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("cache lengths and lookup table must be contiguous int32")
+    return LatentLeaf(paged_cache(pool), _ptr(cache_lengths), _ptr(lookup_table),
+                      lookup_table.shape[1], int(max_cache_length))
+
+
+def msa_latent_partitions(batch: int, max_seq_length: int, num_heads: int, num_latent_heads: int,
+                          window: int, top_c: int, num_partitions: int = 0) -> int:
+    n = library().msa_latent_partitions(batch, max_seq_length, num_heads, num_latent_heads, window,
+                                        top_c, num_partitions)
+    if n < 1:
+        raise MsaError(n, "msa_latent_partitions")
+    return n
+
+
+def msa_latent_workspace_bytes(batch: int, max_seq_length: int, num_heads: int,
+                               num_latent_heads: int, window: int, top_c: int,
+                               num_partitions: int = 0) -> int:
+    return library().msa_latent_workspace_bytes(batch, max_seq_length, num_heads, num_latent_heads,
+                                                window, top_c, num_partitions)
+
+
+def msa_latent_attention_paged(output, q, input_row_offsets, batch: int, max_seq_length: int,
+                               comp_indices, attn_sink, swa: LatentLeaf, comp: LatentLeaf,
+                               num_heads: int, num_latent_heads: int, window: int, scale: float,
+                               num_partitions: int = 0, workspace=None, stream=None):
+    """Fill output [rows, H, 128] (bf16) with latent sparse attention over the
+    window leaf `swa` and the compressed leaf `comp` (either may be None when
+    window, resp. the list length, is 0).  comp_indices int32 [rows, H_lat,
+    top_c] or None; attn_sink float32 [H]."""
+    top_c = 0 if comp_indices is None else comp_indices.shape[-1]
+    if comp_indices is not None and (comp_indices.dtype != torch.int32 or not comp_indices.is_contiguous()):
+        raise ValueError("comp_indices must be contiguous int32")
+    if attn_sink.dtype != torch.float32 or not attn_sink.is_contiguous():
+        raise ValueError("attn_sink must be contiguous float32")
+    need = msa_latent_workspace_bytes(batch, max_seq_length, num_heads, num_latent_heads, window,
+                                      top_c, num_partitions)
+    ws = _workspace(need, q.device, workspace)
+    st = library().msa_latent_attention_paged(
+        _ptr(output), _ptr(q), _ptr(input_row_offsets), batch, max_seq_length, _ptr(comp_indices),
+        top_c, _ptr(attn_sink), None if swa is None else ctypes.byref(swa),
+        None if comp is None else ctypes.byref(comp), num_heads, num_latent_heads, window,
+        float(scale), num_partitions, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "msa_latent_attention_paged")
+    return output
+
+
 # ---------------------------------------------------------------------------
 # convenience: run the whole path on an inputs.Inputs problem
 # ---------------------------------------------------------------------------
@@ -284,3 +355,26 @@ def run_attention(inp, d_indices, output=None, num_partitions: int = 0, workspac
     return msa_attention_paged(output, inp.q, d_indices, inp.k_cache, inp.v_cache, rg,
                                wl.num_q_heads, wl.num_kv_heads, wl.top_k, wl.softmax_scale,
                                num_partitions, workspace, stream)
+
+
+def latent_leaves_of_inputs(inp):
+    """(window leaf, compressed leaf) descriptors of a latent_inputs problem."""
+    wl = inp.wl
+    swa = latent_leaf(inp.swa_pool, inp.swa_cache_lengths, inp.swa_lookup_table,
+                      wl.max_swa_cache_length)
+    comp = latent_leaf(inp.comp_pool, inp.comp_cache_lengths, inp.comp_lookup_table,
+                       wl.max_comp_length)
+    return swa, comp
+
+
+def run_latent(inp, output=None, num_partitions: int = 0, workspace=None, stream=None):
+    wl = inp.wl
+    swa, comp = latent_leaves_of_inputs(inp)
+    if output is None:
+        output = torch.empty((wl.total_rows, wl.num_heads, HEAD_DIM), dtype=torch.bfloat16,
+                             device=inp.q.device)
+    return msa_latent_attention_paged(
+        output, inp.q, inp.input_row_offsets, wl.batch, wl.max_seq_length,
+        inp.comp_indices if wl.top_c > 0 else None, inp.attn_sink,
+        swa if wl.window > 0 else None, comp if wl.top_c > 0 else None, wl.num_heads,
+        wl.num_latent_heads, wl.window, wl.softmax_scale, num_partitions, workspace, stream)

@@ -216,6 +216,67 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
   return MSA_OK;
 }
 
+// ---- latent attention ------------------------------------------------------------
+
+// Column groups of 64 query heads per latent head.
+int latent_col_groups(int G) { return (G + 63) / 64; }
+
+int64_t latent_max_tiles(int32_t window, int32_t top_c) {
+  return ((int64_t)window + top_c + kLatentTile - 1) / kLatentTile;
+}
+
+int check_latent_shape(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                       int32_t num_latent_heads, int32_t window, int32_t top_c, int32_t num_partitions) {
+  if (batch < 0 || max_seq_length < 0) return MSA_ERR_PARAM;
+  if (num_latent_heads < 1 || num_heads < num_latent_heads || num_heads % num_latent_heads)
+    return MSA_ERR_SHAPE;
+  if (window < 0 || window > MSA_LATENT_MAX_WINDOW) return MSA_ERR_PARAM;
+  if (top_c < 0 || top_c > MSA_LATENT_MAX_TOPC) return MSA_ERR_PARAM;
+  if (num_partitions < 0 || num_partitions > kMaxPartitions) return MSA_ERR_PARAM;
+  if ((int64_t)batch * max_seq_length > (int64_t)INT32_MAX / 8) return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+// Partitions: enough that one partition's entries fit the kernel's LDS list;
+// when automatic, enough workgroups for one per CU (the kernel's LDS holds
+// one workgroup per CU), with at least two tiles per partition.
+int plan_latent(int32_t batch, int32_t max_seq_length, int32_t num_heads, int32_t num_latent_heads,
+                int32_t window, int32_t top_c, int32_t req, int cus) {
+  const int64_t tiles = std::max<int64_t>(1, latent_max_tiles(window, top_c));
+  const int64_t per_max = kLatentMaxSlots / kLatentTile;
+  const int64_t min_np = (tiles + per_max - 1) / per_max;
+  if (req > 0) return req >= min_np ? req : MSA_ERR_PARAM;
+  const int64_t base = (int64_t)batch * max_seq_length * num_latent_heads *
+                       latent_col_groups(num_heads / num_latent_heads);
+  int64_t np = ((int64_t)cus + base - 1) / std::max<int64_t>(1, base);
+  np = std::min<int64_t>(np, std::max<int64_t>(1, tiles / 2));
+  np = std::max(np, min_np);
+  return (int)std::min<int64_t>(np, kMaxPartitions);
+}
+
+size_t latent_ws(int32_t batch, int32_t max_seq_length, int32_t num_heads, int np) {
+  if (np <= 1 || batch == 0 || max_seq_length == 0) return 0;
+  const size_t rows = (size_t)np * batch * max_seq_length * num_heads;
+  return align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+int check_latent_leaf(const msa_latent_leaf* lf, int32_t num_latent_heads, int64_t need_entries) {
+  if (!lf) return MSA_ERR_NULL;
+  int st = check_cache(&lf->cache, CacheRole::KV);
+  if (st != MSA_OK) return st;
+  if (lf->cache.num_heads != num_latent_heads) return MSA_ERR_SHAPE;
+  // kernels pack (page, slot) into 32 bits
+  if (lf->cache.num_pages > (1 << 24)) return MSA_ERR_SHAPE;
+  if (!lf->cache_lengths || !lf->lookup_table) return MSA_ERR_NULL;
+  if (lf->max_cache_length < 0) return MSA_ERR_PARAM;
+  if (lf->lookup_stride < 1 || (int64_t)lf->lookup_stride * MSA_BLOCK_SIZE < need_entries) return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+LatentLeaf leaf_of(const msa_latent_leaf* lf) {
+  return LatentLeaf{pool_of(lf->cache), lf->cache_lengths, lf->lookup_table, lf->lookup_stride};
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +370,103 @@ int msa_indexer_reuse(int32_t* d_indices, const int32_t* prev_indices, const int
   if (launch_indexer_reuse(d_indices, prev_indices, src_row, rows, prev_rows,
                            num_kv_heads * top_k, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MSA_ERR_LAUNCH;
+  return MSA_OK;
+}
+
+int msa_latent_partitions(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                          int32_t num_latent_heads, int32_t window, int32_t top_c,
+                          int32_t num_partitions) {
+  int st = check_latent_shape(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
+                              num_partitions);
+  if (st != MSA_OK) return st;
+  int cus = 256;
+  if (num_partitions == 0 && current_device(&cus) != MSA_OK) cus = 256;
+  return plan_latent(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
+                     num_partitions, cus);
+}
+
+size_t msa_latent_workspace_bytes(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                                  int32_t num_latent_heads, int32_t window, int32_t top_c,
+                                  int32_t num_partitions) {
+  const int np = msa_latent_partitions(batch, max_seq_length, num_heads, num_latent_heads, window,
+                                       top_c, num_partitions);
+  if (np < 1) return 0;
+  return latent_ws(batch, max_seq_length, num_heads, np);
+}
+
+int msa_latent_attention_paged(void* output, const void* q, const int32_t* input_row_offsets,
+                               int32_t batch, int32_t max_seq_length, const int32_t* comp_indices,
+                               int32_t top_c, const float* attn_sink, const msa_latent_leaf* swa,
+                               const msa_latent_leaf* comp, int32_t num_heads,
+                               int32_t num_latent_heads, int32_t window, float scale,
+                               int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int st = check_latent_shape(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
+                              num_partitions);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale > 3.0e38f) return MSA_ERR_PARAM;   // positive and finite
+  if (batch == 0 || max_seq_length == 0) return MSA_OK;
+  if (!output || !q || !input_row_offsets || !attn_sink) return MSA_ERR_NULL;
+  if (!aligned16(output) || !aligned16(q)) return MSA_ERR_SHAPE;
+  if (window > 0) {
+    if (!swa) return MSA_ERR_NULL;
+    if ((st = check_latent_leaf(swa, num_latent_heads,
+                                (int64_t)swa->max_cache_length + max_seq_length)) != MSA_OK)
+      return st;
+  }
+  if (top_c > 0) {
+    if (!comp || !comp_indices) return MSA_ERR_NULL;
+    if ((st = check_latent_leaf(comp, num_latent_heads, comp->max_cache_length)) != MSA_OK) return st;
+  }
+  // the kernel's tile format is BF16
+  if ((window > 0 && swa->cache.dtype != MSA_DTYPE_BF16) ||
+      (top_c > 0 && comp->cache.dtype != MSA_DTYPE_BF16))
+    return MSA_ERR_DTYPE;
+  int cus = 0;
+  if (num_partitions == 0 && (st = current_device(&cus)) != MSA_OK) return st;
+  const int np = plan_latent(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
+                             num_partitions, cus);
+  if (np < 1) return np;
+  const size_t need = latent_ws(batch, max_seq_length, num_heads, np);
+  if (need && !workspace) return MSA_ERR_NULL;
+  if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  const int ncg = latent_col_groups(num_heads / num_latent_heads);
+  if ((int64_t)batch * max_seq_length * num_latent_heads * ncg * np > (int64_t)INT32_MAX)
+    return MSA_ERR_SHAPE;
+  if (num_partitions != 0 && (st = current_device(&cus)) != MSA_OK) return st;
+
+  LatentParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.offs = input_row_offsets;
+  p.batch = batch;
+  p.max_seq = max_seq_length;
+  p.lists = comp_indices;
+  p.top_c = top_c;
+  p.sink = attn_sink;
+  if (window > 0) p.swa = leaf_of(swa);
+  if (top_c > 0) p.comp = leaf_of(comp);
+  p.H = num_heads;
+  p.H_lat = num_latent_heads;
+  p.G = num_heads / num_latent_heads;
+  p.ncg = ncg;
+  p.window = window;
+  p.np = np;
+  p.rcap = batch * max_seq_length;
+  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  p.out = static_cast<uint16_t*>(output);
+  if (np > 1) {
+    const size_t rows = (size_t)np * p.rcap * num_heads;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align_up(rows * MSA_HEAD_DIM * sizeof(float)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_latent(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  if (np > 1) {
+    CombineParams c{p.part_o, p.part_lse, input_row_offsets, p.out, batch, max_seq_length, np,
+                    num_heads, p.rcap};
+    if (launch_combine(c, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  }
   return MSA_OK;
 }
 

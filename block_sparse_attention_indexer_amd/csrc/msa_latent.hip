@@ -1,0 +1,388 @@
+// Latent sparse attention ("Struct_latent_sparse_attention_ragged_paged" page
+// of the MAX Mojo docs): every cached entry is one latent vector that is both
+// key and value, read from a sliding-window leaf (a range of positions) and a
+// compressed leaf (a per-query list of entries), with a per-head sink logit
+// in the softmax denominator.
+//
+// One workgroup of four waves owns (row, latent head, group of up to 64
+// query heads, split-K partition).  The row's entries are numbered window
+// positions first, then list slots; a partition takes a contiguous run of
+// 32-entry tiles of that numbering.  The workgroup first resolves each of
+// its entries to the address of its latent vector (in LDS).  The waves then
+// take the partition's tiles in turn (wave w: tiles w, w + 4, ...), each
+// streaming its own tiles through its own ring of LDS stages with
+// global->LDS DMA, three tiles in flight, so no wave waits for another
+// inside the loop.  A wave holds all of the group's query heads as MFMA
+// columns (up to four 16-column tiles): S^T = X . Q^T over a tile (X the
+// 32 latent rows), an online softmax over the rows, then O^T += X^T . P^T
+// with X^T read from the same LDS tile by transposing reads -- keys and
+// values are one tile, fetched once, and every operand read feeds one MFMA
+// per column tile.  At the end the four waves' softmax states are merged
+// through LDS.
+//
+// The tile is stored row-major, 256 bytes per entry, with 16-byte column c
+// of row pos at c ^ f(pos), f(pos) = ((pos & 7) << 1) | ((pos >> 3) & 1),
+// which keeps the transposing value reads free of LDS bank conflicts (the
+// 16-byte key reads measure 2-way conflicted with it).
+//
+// Entries a partition does not attend (a list value outside [0, leaf
+// length), the padding after the row's last entry) are still fetched -- from
+// the row's own query vector, a finite stand-in -- so that every wave issues
+// the same number of DMAs per tile and the vmcnt waits stay exact; their
+// scores are masked to -inf, so their probability is exactly 0.
+//
+// The sink joins one wave's running softmax in partition 0 as one more
+// logit with no value (max = sink, sum = 1 before any entry), so neither the
+// merge nor the split-K combine needs anything extra.
+#include <algorithm>
+
+#include "msa_common.h"
+#include "msa_kernels.h"
+#include "msa_lds.h"
+
+namespace msa {
+
+constexpr int kLatWaves = 4;
+constexpr int kLatRowBytes = 256;                              // one BF16 latent vector
+constexpr int kLatTileBytes = kLatentTile * kLatRowBytes;      // 8 KiB
+constexpr int kLatStages = 4;                                  // per wave
+constexpr int kLatDma = kLatTileBytes / 1024;                  // DMAs per tile: 8
+constexpr float kLatLazy = 8.f;   // log2 headroom before the running max moves
+
+struct LatentLds {
+  // per-wave tile rings; after the loop, each wave's merged-state area
+  char ring[kLatWaves][kLatStages * kLatTileBytes];
+  // first byte of each entry's latent vector, or null: not attended; after
+  // the loop, the waves' per-column max and sum
+  const char* src[kLatentMaxSlots];
+};
+
+__device__ __forceinline__ int lat_swz(int pos) { return ((pos & 7) << 1) | ((pos >> 3) & 1); }
+
+template <int NCT>
+__global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentParams p) {
+  __shared__ __attribute__((aligned(16))) LatentLds L;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = uniform((int)(tid >> 6));
+  const int l16 = lane & 15, g = lane >> 4;
+
+  int id = blockIdx.x;
+  const int pi = id % p.np;
+  id /= p.np;
+  const int cg = id % p.ncg;
+  id /= p.ncg;
+  const int hl = id % p.H_lat;
+  id /= p.H_lat;
+  const int b = id / p.max_seq, t = id % p.max_seq;
+  // the sequence's lengths are read together with its row offsets (one
+  // memory round trip, not two)
+  const int r0 = p.offs[b], r1 = p.offs[b + 1];
+  const int swa_len = p.window > 0 ? p.swa.clen[b] : 0;
+  const int comp_len = p.top_c > 0 ? p.comp.clen[b] : 0;
+  if (t >= min(r1 - r0, p.max_seq)) return;
+  const int r = r0 + t;
+
+  // ---- queries: the group's heads as NCT 16-column MFMA tiles -------------------
+  const uint16_t* qrow = p.q + (size_t)r * p.H * kDim;
+  u32x4 qf[NCT][4];
+  bool col_ok[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int hcol = cg * 64 + 16 * ct + l16;
+    col_ok[ct] = hcol < p.G;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qf[ct][s] = col_ok[ct] ? ld16(qrow + (size_t)(hl * p.G + hcol) * kDim + 32 * s + 8 * g)
+                             : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- this partition's entries ---------------------------------------------
+  const int pos = swa_len + t;
+  const int n_swa = p.window > 0 ? min(p.window, pos + 1) : 0;
+  const int lo = pos - n_swa + 1;
+  const int nent = n_swa + p.top_c;
+  const int ntiles_row = (nent + kLatentTile - 1) / kLatentTile;
+  const int e0 = (int)((int64_t)ntiles_row * pi / p.np);
+  const int e1 = (int)((int64_t)ntiles_row * (pi + 1) / p.np);
+  const int ntile = e1 - e0;
+  const int s0 = e0 * kLatentTile;
+  const int s1 = min(nent, e1 * kLatentTile);
+  const int32_t* lst = p.lists + ((size_t)r * p.H_lat + hl) * p.top_c;
+  // Resolve every entry of the partition to the address of its latent
+  // vector.  Every load is issued unconditionally (slots that need none read
+  // a harmless int instead) and the loaded values are merged with masks, not
+  // branches, so a thread's loads are all in flight together: the partition
+  // pays two memory round trips, not two per entry.
+  {
+    constexpr int kPer = kLatentMaxSlots / (64 * kLatWaves);
+    const int32_t* swa_tab = p.swa.table + (size_t)b * p.swa.stride;
+    const int32_t* comp_tab = p.comp.table + (size_t)b * p.comp.stride;
+    const char* swa_base = static_cast<const char*>(p.swa.pool.data);
+    const char* comp_base = static_cast<const char*>(p.comp.pool.data);
+    if (swa_base) swa_base += (size_t)hl * p.swa.pool.head_stride * 2;
+    if (comp_base) comp_base += (size_t)hl * p.comp.pool.head_stride * 2;
+    int ent[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = s0 + tid + 64 * kLatWaves * k;
+      const bool listed = s < s1 && s >= n_swa;
+      const int v = *(listed ? lst + (s - n_swa) : p.offs);
+      const int m = -(int)listed;
+      ent[k] = (v & m) | ((s < n_swa ? lo + s : -1) & ~m);
+    }
+    int pg[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = s0 + tid + 64 * kLatWaves * k;
+      const int e = ent[k];
+      const bool win = s < s1 && s < n_swa;
+      const bool cmp = s < s1 && s >= n_swa && e >= 0 && e < comp_len;
+      const int v = *(win ? swa_tab + (e >> 7) : cmp ? comp_tab + (e >> 7) : p.offs);
+      const int m = -(int)(win || cmp);
+      pg[k] = (v & m) | ~m;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = s0 + tid + 64 * kLatWaves * k;
+      const int i = tid + 64 * kLatWaves * k;
+      if (i < ntile * kLatentTile) {
+        const char* a = nullptr;
+        if (pg[k] >= 0)
+          a = s < n_swa ? swa_base + (size_t)pg[k] * p.swa.pool.page_stride * 2 +
+                              (size_t)(ent[k] & 127) * p.swa.pool.token_stride * 2
+                        : comp_base + (size_t)pg[k] * p.comp.pool.page_stride * 2 +
+                              (size_t)(ent[k] & 127) * p.comp.pool.token_stride * 2;
+        L.src[i] = a;
+      }
+    }
+  }
+
+  f32x4 O[8][NCT];
+  float m_run[NCT], l_run[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = neg_inf();
+    l_run[ct] = 0.f;
+    if (pi == 0 && wave == 0 && col_ok[ct]) {
+      const float sk = p.sink[hl * p.G + cg * 64 + 16 * ct + l16];
+      if (sk != neg_inf()) {
+        m_run[ct] = sk * kLog2e;
+        l_run[ct] = g == 0 ? 1.f : 0.f;   // counted once per column
+      }
+    }
+  }
+  const float sc = p.scale_log2;
+  // every load so far has landed before the first DMA is issued, so that the
+  // compiler's own waits for them never have to drain the tile ring
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // ---- this wave's tiles ----------------------------------------------------------
+  // DMA i of a tile fetches rows 4i .. 4i + 3; lane (l16, g) lands in row
+  // 4i + g at physical column l16, which holds logical column l16 ^ f(row).
+  // Rows that are not attended fetch 16 bytes of the row's first query
+  // vector instead.
+  char* ring = L.ring[wave];
+  const int my_n = ntile > wave ? (ntile - wave + kLatWaves - 1) / kLatWaves : 0;
+  const char* dummy = reinterpret_cast<const char*>(qrow) + 16 * l16;
+  uint32_t colb[kLatDma];
+#pragma unroll
+  for (int i = 0; i < kLatDma; ++i) colb[i] = (uint32_t)((l16 ^ lat_swz(4 * i + g)) << 4);
+  auto issue = [&](int j) {
+    const int tb = (wave + kLatWaves * j) * kLatentTile;
+    char* stage = ring + (j % kLatStages) * kLatTileBytes;
+    const char* a[kLatDma];
+#pragma unroll
+    for (int i = 0; i < kLatDma; ++i) a[i] = L.src[tb + 4 * i + g];
+#pragma unroll
+    for (int i = 0; i < kLatDma; ++i) dma16(a[i] ? a[i] + colb[i] : dummy, stage + 4 * i * kLatRowBytes);
+  };
+
+  // lane-constant LDS offsets.  K A-operand: row 16pt + l16, logical column
+  // 4s + g.  X^T A-operand (transposing read h, dim tile dt): source lane
+  // (l16, g) reads row 16h + 4g + l16 / 4 at dims 16dt + 4(l16 % 4), so
+  // output lane (m, g) receives dim 16dt + m of rows 16h + 4g + k -- the
+  // P^T B-operand layout.
+  const int kq = l16 * kLatRowBytes + ((g ^ lat_swz(l16)) << 4);
+  const int vrow = 4 * g + (l16 >> 2);
+  const int vq = vrow * kLatRowBytes + ((((l16 & 3) >> 1) ^ lat_swz(vrow)) << 4) + 8 * (l16 & 1);
+
+#pragma unroll
+  for (int j = 0; j < kLatStages - 1; ++j)
+    if (j < my_n) issue(j);
+
+  for (int j = 0; j < my_n; ++j) {
+    // this wave's DMAs of tile j are done once at most those of the younger
+    // tiles in flight remain (the wave reads only what it fetched itself)
+    const int younger = min(my_n - 1 - j, kLatStages - 2);
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLatDma));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLatDma));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // the stage of tile j - 1 is free: this wave's reads of it have returned
+    if (j + kLatStages - 1 < my_n) issue(j + kLatStages - 1);
+
+    const char* tile = ring + (j % kLatStages) * kLatTileBytes;
+    // The key operands are requested together (one LDS latency per tile);
+    // the transposed value reads are issued right behind the score MFMAs, so
+    // they land while the scores and the softmax run.  (LDS results return
+    // in order and the wait counter saturates at 15, so requesting the
+    // values first would make the first MFMA wait for them.)
+    u32x4 ka[2][4];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        ka[pt][s] = *reinterpret_cast<const u32x4*>(tile + 16 * pt * kLatRowBytes + (kq ^ (s << 6)));
+    const int tb = (wave + kLatWaves * j) * kLatentTile;
+    const uint32_t live = (uint32_t)ballot(lane < kLatentTile && L.src[tb + (lane & 31)] != nullptr);
+    // this lane's rows of the tile are 16pt + 4g + i: bit 4pt + i of m8
+    const uint32_t lg = live >> (4 * g);
+    const uint32_t m8 = (lg & 0xFu) | ((lg >> 12) & 0xF0u);
+    const bool full = live == 0xFFFFFFFFu;
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 S[2][NCT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          S[pt][ct] = mfma_bf16(ka[pt][s], qf[ct][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[pt][ct]);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x2 va[8][2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const char* base = tile + (vq ^ (dt << 5));
+      va[dt][0] = lds_tr_b16(base);
+      va[dt][1] = lds_tr_b16(base + 16 * kLatRowBytes);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (!full) {
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((m8 >> (4 * pt + i)) & 1u))
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) S[pt][ct][i] = neg_inf();
+    }
+    bool any_move = false;
+    float alpha[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float hmax = fmaxf(fmaxf(fmaxf(S[0][ct][0], S[0][ct][1]), fmaxf(S[0][ct][2], S[0][ct][3])),
+                         fmaxf(fmaxf(S[1][ct][0], S[1][ct][1]), fmaxf(S[1][ct][2], S[1][ct][3])));
+      hmax = colgroup_max(hmax) * sc;
+      // lazy rescaling: the reference max only moves when a score would
+      // exceed it by more than 2^kLatLazy
+      const bool move = col_ok[ct] && hmax > m_run[ct] + kLatLazy;
+      const float m_new = move ? hmax : m_run[ct];
+      const float m_use = m_new == neg_inf() ? 0.f : m_new;
+      const float off = col_ok[ct] ? m_use : __builtin_inff();
+      alpha[ct] = move ? fast_exp2(m_run[ct] - m_use) : 1.f;
+      any_move |= move;
+      float lsum = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e2 = fast_exp2(__builtin_fmaf(S[pt][ct][i], sc, -off));
+          S[pt][ct][i] = e2;
+          lsum += e2;
+        }
+      l_run[ct] = l_run[ct] * alpha[ct] + lsum;
+      m_run[ct] = m_new;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_move)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) O[dt][ct] *= alpha[ct];
+    }
+    u32x4 bp[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      bp[ct] = u32x4{pack_bf16(S[0][ct][0], S[0][ct][1]), pack_bf16(S[0][ct][2], S[0][ct][3]),
+                     pack_bf16(S[1][ct][0], S[1][ct][1]), pack_bf16(S[1][ct][2], S[1][ct][3])};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x4 a = {va[dt][0].x, va[dt][0].y, va[dt][1].x, va[dt][1].y};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = mfma_bf16(a, bp[ct], O[dt][ct]);
+    }
+  }
+
+  // ---- merge the four waves' states ------------------------------------------
+  // Wave w stores its column max and sum (src area) and its unnormalised O
+  // (its ring, [ct][dt][lane] f32x4); wave ct then merges column tile ct:
+  // M = max_w m_w, O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
+  float l_tot[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) l_tot[ct] = colgroup_sum(l_run[ct]);
+  __syncthreads();   // every wave is done with its ring and the entry list
+  float* stat = reinterpret_cast<float*>(L.src);                  // [w][ct][2][16]
+  f32x4* ow = reinterpret_cast<f32x4*>(L.ring[wave]);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) ow[(ct * 8 + dt) * 64 + lane] = O[dt][ct];
+    if (g == 0) {
+      stat[((wave * NCT + ct) * 2 + 0) * 16 + l16] = m_run[ct];
+      stat[((wave * NCT + ct) * 2 + 1) * 16 + l16] = l_tot[ct];
+    }
+  }
+  __syncthreads();
+  if (wave >= NCT) return;
+  const int ct = wave;
+  if (!col_ok[ct]) return;
+  float mw[kLatWaves], M = neg_inf();
+#pragma unroll
+  for (int w = 0; w < kLatWaves; ++w) {
+    mw[w] = stat[((w * NCT + ct) * 2 + 0) * 16 + l16];
+    M = fmaxf(M, mw[w]);
+  }
+  float lsum = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kLatWaves; ++w) {
+    const float sw = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
+    lsum += sw * stat[((w * NCT + ct) * 2 + 1) * 16 + l16];
+    const f32x4* src = reinterpret_cast<const f32x4*>(L.ring[w]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] += sw * src[(ct * 8 + dt) * 64 + lane];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+
+  // ---- store: O^T tile dt, C row 4g + i is dim 16dt + 4g + i ----------------------
+  const size_t hrow = (size_t)r * p.H + hl * p.G + cg * 64 + 16 * ct + l16;
+  if (p.np == 1) {
+    uint16_t* op = p.out + hrow * kDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<u32x2*>(op + 16 * dt) =
+          u32x2{pack_bf16(o[dt][0] * inv, o[dt][1] * inv), pack_bf16(o[dt][2] * inv, o[dt][3] * inv)};
+  } else {
+    const size_t prow = (size_t)pi * p.rcap * p.H + hrow;
+    float* op = p.part_o + prow * kDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt) = o[dt] * inv;
+    if (g == 0) p.part_lse[prow] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : neg_inf();
+  }
+}
+
+hipError_t launch_latent(const LatentParams& p, hipStream_t s) {
+  const size_t nwg = (size_t)p.batch * p.max_seq * p.H_lat * p.ncg * p.np;
+  const int cols = std::min(64, p.G - 0);   // heads of the widest column group
+  const dim3 grid((unsigned)nwg), block(64 * kLatWaves);
+  if (cols <= 16) hipLaunchKernelGGL(latent_attn_kernel<1>, grid, block, 0, s, p);
+  else if (cols <= 32) hipLaunchKernelGGL(latent_attn_kernel<2>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(latent_attn_kernel<4>, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace msa

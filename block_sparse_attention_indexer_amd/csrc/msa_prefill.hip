@@ -22,6 +22,7 @@
 
 #include "msa_common.h"
 #include "msa_kernels.h"
+#include "msa_lds.h"
 
 namespace msa {
 
@@ -30,34 +31,6 @@ __device__ __forceinline__ int k_off(int pos, int c16) { return pos * 256 + ((c1
 __device__ __forceinline__ u32x4 lds16(const char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
-
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Global -> LDS copy of 16 bytes per lane: lane L's bytes land at lds_dst +
-// 16 L (lds_dst is wave-uniform).  Written as inline asm (M0 = LDS address,
-// one wait state, the DMA; no register outputs) rather than the builtin,
-// because the compiler treats a builtin DMA as a pending LDS write and waits
-// for every one of them before any later LDS read, which would drain the
-// tile ring on every block.  The callers order each stage's reads after its
-// DMA themselves: an explicit vmcnt wait for this wave's own DMA, then a
-// workgroup barrier for everyone else's.
-// M0 is reserved to the compiler, which warns about the clobber; nothing in
-// these kernels keeps a value in M0 across a DMA (every M0 write in the
-// generated code is the one above its DMA).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
-  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)(lds_char*)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_addr)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt immediate that waits until at most n of this wave's vector-memory
-// operations are outstanding (lgkm and exp counters not waited on).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // ---------------------------------------------------------------------------
 // Work lists.  The prefill grids would otherwise be over-launched from host
@@ -488,21 +461,6 @@ struct PrefillLds3 {
   int32_t ring_blk[2 * kRingHalf], ring_pg[2 * kRingHalf];
   uint32_t ring_msk[2 * kRingHalf];
 };
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-
-// 8-byte transposing LDS reads of 16-bit and of 8-bit elements
-__device__ __forceinline__ u32x2 lds_tr_b16(const char* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
-__device__ __forceinline__ u32x2 lds_tr_b8(const char* p) {
-  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_char*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
 
 // FP8 tile swizzles (16-byte column XOR masks of row pos)
 __device__ __forceinline__ int fp8_vswz(int pos) {

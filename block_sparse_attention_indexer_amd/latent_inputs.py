@@ -157,7 +157,8 @@ def make_latent_inputs(wl: LatentWorkload, device="cpu") -> LatentInputs:
     nan = float("nan")
 
     # window leaf: the logical pages some new token's window reaches
-    swa_stride = max(1, max((c + n + PAGE - 1) // PAGE for c, n in zip(wl.swa_cache_lens, wl.new_lens)))
+    # the table covers the host bounds: max cached positions + max new tokens
+    swa_stride = max(1, (wl.max_swa_cache_length + wl.max_seq_length + PAGE - 1) // PAGE)
     spans = [wl.window_span(b) for b in range(B)]
     swa_need = [list(range(lo // PAGE, hi // PAGE + 1)) if hi >= lo else [] for lo, hi in spans]
     n_swa = sum(len(x) for x in swa_need)

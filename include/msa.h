@@ -282,6 +282,96 @@ int msa_splitk_combine(void* output, const float* partial_o, const float* partia
                        int32_t max_seq_length, int32_t num_partitions,
                        int32_t num_q_heads, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Latent sparse attention                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The second operation of the family: the mo.latent_sparse_attention.
+ * ragged.paged graph op ("Struct_latent_sparse_attention_ragged_paged" page
+ * of the MAX Mojo docs, struct summary and the execute argument list).  One
+ * latent vector per cached entry is both key and value; entries come from
+ * two paged leaves, a sliding-window leaf read by a range of positions and
+ * a compressed leaf read through an explicit list of entries per query; a
+ * per-head attention sink enters the softmax denominator.
+ *
+ * One leaf as the operation sees it: its page pool (head_dim 128, 128
+ * entries per page, num_heads = latent heads, BF16 or scale-free FP8 e4m3,
+ * scale NULL) and how the sequences map into it.  Entry i of sequence b is
+ * slot i % 128 of page lookup_table[b * lookup_stride + i / 128]; the page's
+ * layer is chosen by passing that layer's pool.
+ */
+typedef struct msa_latent_leaf {
+    msa_paged_cache cache;
+    const int32_t* cache_lengths;  /* device [batch]                              */
+    const int32_t* lookup_table;   /* device [batch][lookup_stride]: page ids     */
+    int32_t lookup_stride;         /* entries per sequence in the table           */
+    int32_t max_cache_length;      /* host bound on cache_lengths[b]              */
+} msa_latent_leaf;
+
+enum {
+    MSA_LATENT_MAX_TOPC = 16384,   /* most list slots per (row, latent head)     */
+    MSA_LATENT_MAX_WINDOW = 1 << 20
+};
+
+/* Split-K partitions msa_latent_attention_paged uses for this shape when
+ * called with num_partitions (0 = automatic choice that fills the GPU).
+ * Returns a negative MSA_ERR_* code on invalid arguments. */
+int msa_latent_partitions(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                          int32_t num_latent_heads, int32_t window, int32_t top_c,
+                          int32_t num_partitions);
+
+/* Workspace bytes msa_latent_attention_paged needs (split-K partials when
+ * more than one partition is used).  Returns 0 on invalid arguments. */
+size_t msa_latent_workspace_bytes(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                                  int32_t num_latent_heads, int32_t window, int32_t top_c,
+                                  int32_t num_partitions);
+
+/*
+ * For row r = input_row_offsets[b] + t (new token t of sequence b, at
+ * window-leaf position p = swa->cache_lengths[b] + t) and query head g of
+ * latent head hl = g / (num_heads / num_latent_heads):
+ *   W = window-leaf positions max(0, p - window + 1) .. p  (none if window 0)
+ *   C = the values e of comp_indices[r][hl][0 .. top_c) with
+ *       0 <= e < comp->cache_lengths[b], each occurrence counted
+ *   z_j = scale * q[r][g] . x_j for every latent vector x_j of W and C
+ *   out[r][g] = sum_j exp(z_j) x_j / (sum_j exp(z_j) + exp(attn_sink[g]))
+ * with FP32 accumulation, rounded to BF16 (round to nearest even).  A sink
+ * of -inf means no sink; a row with nothing to attend gets 0.  Sinks must be
+ * finite or -inf, attended latent values finite.
+ *
+ * output            device bf16 [rows][num_heads][128]; rows >=
+ *                   input_row_offsets[batch] are not written.
+ * q                 device bf16 [rows][num_heads][128].
+ * input_row_offsets device int32 [batch + 1].
+ * max_seq_length    host bound on new tokens per sequence.
+ * comp_indices      device int32 [rows][num_latent_heads][top_c]; may be
+ *                   NULL when top_c == 0.
+ * attn_sink         device float32 [num_heads].
+ * swa, comp         the two leaves (num_heads == num_latent_heads in both);
+ *                   swa may be NULL when window == 0, comp when top_c == 0.
+ *                   swa->lookup_stride must cover positions up to
+ *                   swa->max_cache_length + max_seq_length - 1, and
+ *                   comp->lookup_stride entries up to comp->max_cache_length - 1.
+ * num_heads         a multiple of num_latent_heads (any group size).
+ * window            0 .. MSA_LATENT_MAX_WINDOW; top_c 0 .. MSA_LATENT_MAX_TOPC.
+ * scale             positive and finite.
+ * num_partitions    0 = automatic, else 1 .. 64.
+ * workspace         device, >= msa_latent_workspace_bytes(...) bytes.
+ *
+ * Errors: MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_PARAM, MSA_ERR_DTYPE,
+ * MSA_ERR_WORKSPACE, MSA_ERR_LAUNCH, MSA_ERR_DEVICE.  batch == 0 is a no-op.
+ * When more than one partition is used the call enqueues the combine itself.
+ */
+int msa_latent_attention_paged(void* output, const void* q, const int32_t* input_row_offsets,
+                               int32_t batch, int32_t max_seq_length,
+                               const int32_t* comp_indices, int32_t top_c,
+                               const float* attn_sink, const msa_latent_leaf* swa,
+                               const msa_latent_leaf* comp, int32_t num_heads,
+                               int32_t num_latent_heads, int32_t window, float scale,
+                               int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* msa_status_string(int status);
 

@@ -24,10 +24,12 @@ def test_library_exports_every_declared_function():
 def test_binding_constants_match_header():
     text = open(B.HEADER).read()
     for name in ("MSA_MAX_SPEC_DRAFT", "MSA_MAX_BLOCKS", "MSA_MAX_TOPK", "MSA_DTYPE_BF16",
-                 "MSA_DTYPE_FP8_E4M3"):
+                 "MSA_DTYPE_FP8_E4M3", "MSA_LATENT_MAX_TOPC"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m, name
         assert int(m.group(1)) == getattr(B, name), name
+    m = re.search(r"\bMSA_LATENT_MAX_WINDOW\s*=\s*1\s*<<\s*(\d+)", text)
+    assert m and 1 << int(m.group(1)) == B.MSA_LATENT_MAX_WINDOW
 
 
 def rg(batch=2, max_seq=1, max_cache=4000, stride=40, null=False):
@@ -156,3 +158,61 @@ def test_combine_validation():
     assert lib.msa_splitk_combine(FAKE, FAKE, FAKE, FAKE, 2, 1, 0, 8, None) == PARAM
     assert lib.msa_splitk_combine(None, FAKE, FAKE, FAKE, 2, 1, 2, 8, None) == NULL
     assert lib.msa_splitk_combine(FAKE, FAKE, FAKE, FAKE, 0, 1, 2, 8, None) == OK
+
+
+def leaf(heads=1, stride=40, max_cache=4000, dtype=B.MSA_DTYPE_BF16, null_table=False, pages=100):
+    c = cache(dtype=dtype, heads=heads)
+    c.num_pages = pages
+    return B.LatentLeaf(c, FAKE, None if null_table else FAKE, stride, max_cache)
+
+
+def latent(swa, comp, batch=2, max_seq=1, top_c=512, heads=64, lat=1, window=128, np_=2, ws=1 << 30,
+           scale=0.1, out=FAKE, lists=FAKE, sink=FAKE):
+    return B.library().msa_latent_attention_paged(
+        out, FAKE, FAKE, batch, max_seq, lists, top_c, sink,
+        None if swa is None else ctypes.byref(swa), None if comp is None else ctypes.byref(comp),
+        heads, lat, window, scale, np_, FAKE if ws else None, ws, None)
+
+
+def test_latent_validation():
+    """Every check runs before a device query, so a valid call here would only
+    fail at the device lookup (-7) -- each case below fails earlier."""
+    s, c = leaf(), leaf(stride=40)
+    assert latent(s, c, out=None) == NULL
+    assert latent(s, c, sink=None) == NULL
+    assert latent(None, c) == NULL                             # window > 0 needs the window leaf
+    assert latent(s, None) == NULL                             # a list needs the compressed leaf
+    assert latent(s, c, lists=None) == NULL
+    assert latent(s, leaf(null_table=True)) == NULL
+    assert latent(s, c, heads=60, lat=8) == SHAPE              # not a multiple
+    assert latent(s, c, lat=2) == SHAPE                        # leaves hold one latent head
+    assert latent(leaf(stride=31), c) == SHAPE                 # table too short for the window leaf
+    assert latent(s, leaf(stride=31, max_cache=4000)) == SHAPE
+    assert latent(leaf(pages=(1 << 24) + 1), c) == SHAPE
+    assert latent(s, c, window=-1) == PARAM
+    assert latent(s, c, window=(1 << 20) + 1) == PARAM
+    assert latent(s, c, top_c=16385) == PARAM
+    assert latent(s, c, np_=65) == PARAM
+    assert latent(s, c, scale=0.0) == PARAM
+    assert latent(s, c, scale=float("nan")) == PARAM
+    assert latent(leaf(dtype=7), c) == DTYPE
+    assert latent(s, leaf(dtype=B.MSA_DTYPE_FP8_E4M3)) == DTYPE   # FP8 leaves not built
+    need = B.msa_latent_workspace_bytes(2, 1, 64, 1, 128, 512, 2)
+    assert need >= 2 * 2 * 64 * 129 * 4
+    assert latent(s, c, ws=need - 1) == WORKSPACE
+    assert latent(s, c, ws=0) == NULL
+    assert latent(s, c, batch=0) == OK
+    # window 0 and no list: neither leaf is needed
+    assert latent(None, None, window=0, top_c=0, lists=None, np_=1, ws=0) not in (NULL, SHAPE, PARAM)
+
+
+def test_latent_partition_planning():
+    # one partition's entries must fit 2048 list slots: 10 000 entries need >= 5
+    assert B.library().msa_latent_partitions(4, 1, 64, 1, 128, 9872, 4) == PARAM
+    assert B.msa_latent_partitions(4, 1, 64, 1, 128, 9872, 5) == 5
+    assert B.msa_latent_partitions(4, 1, 64, 1, 128, 9872, 0) >= 5
+    assert B.msa_latent_partitions(64, 1, 64, 1, 128, 1920, 1) == 1    # 32 tiles fit one
+    assert B.msa_latent_workspace_bytes(64, 1, 64, 1, 128, 1920, 1) == 0
+    assert B.library().msa_latent_partitions(64, 1, 64, 1, 128, 1921, 1) == PARAM
+    with pytest.raises(B.MsaError):
+        B.msa_latent_partitions(4, 1, 64, 3, 128, 16, 0)
