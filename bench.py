@@ -226,7 +226,8 @@ def kernel_of(workload):
 
 def kernel_source_hash(workload="decode_batch64"):
     h = hashlib.sha256()
-    files = (("msa_latent.hip", "msa_lds.h", "msa_attention.hip", "msa_common.h", "msa_kernels.h")
+    files = (("msa_latent.hip", "msa_latent.h", "msa_lds.h", "msa_attention.hip", "msa_common.h",
+              "msa_kernels.h")
              if is_latent(workload) else ("msa_attention.hip", "msa_common.h", "msa_kernels.h"))
     for f in files:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc", f), "rb").read())

@@ -15,6 +15,7 @@
 
 #include "msa.h"
 #include "msa_kernels.h"
+#include "msa_latent.h"
 
 namespace {
 

@@ -78,37 +78,6 @@ struct CombineParams {
   int32_t batch, max_seq, np, H_q, rcap;
 };
 
-// One leaf of the latent cache: its pool and how sequences map into it.
-struct LatentLeaf {
-  Pool pool;
-  const int32_t* clen;    // [B] entries (window leaf: positions) cached
-  const int32_t* table;   // [B][stride] page ids
-  int32_t stride;
-};
-
-struct LatentParams {
-  const uint16_t* q;      // bf16 [R][H][128]
-  const int32_t* offs;    // [B+1]
-  int32_t batch, max_seq;
-  const int32_t* lists;   // [R][H_lat][top_c] compressed-leaf entries
-  int32_t top_c;
-  const float* sink;      // [H]
-  LatentLeaf swa, comp;
-  int32_t swa_fp8, comp_fp8;
-  int32_t H, H_lat, G;    // query heads, latent heads, query heads per latent head
-  int32_t ncg;            // column groups of 64 query heads per latent head
-  int32_t window, np, rcap;
-  float scale_log2;       // softmax scale * log2(e)
-  uint16_t* out;          // bf16 [R][H][128]
-  float* part_o;          // [np][rcap][H][128]
-  float* part_lse;        // [np][rcap][H]
-};
-
-// Most list slots (entries) one partition of a latent row may hold.
-constexpr int kLatentMaxSlots = 2048;
-// Entries per latent tile.
-constexpr int kLatentTile = 32;
-
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_t s);
 // out[r][:] = prev[src[r]][:] (row length `width` ints), -1 rows for sources
@@ -121,7 +90,6 @@ hipError_t launch_topk(const IndexerParams& p, hipStream_t s);
 hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s);
-hipError_t launch_latent(const LatentParams& p, hipStream_t s);
 
 // Tokens per tile (tq) and MFMA column tiles per wave of the prefill
 // attention for group size G and KV storage type.

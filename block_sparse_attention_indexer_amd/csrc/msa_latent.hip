@@ -38,6 +38,7 @@
 
 #include "msa_common.h"
 #include "msa_kernels.h"
+#include "msa_latent.h"
 #include "msa_lds.h"
 
 namespace msa {
