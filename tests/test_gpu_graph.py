@@ -84,3 +84,59 @@ def test_graph_replay_matches_eager(case):
             f"{case} replay {rep}: output differs from eager"
         assert torch.isfinite(out_g.float()).all()
     print(f"  {case}: 3 replays identical to eager (np={np_})", flush=True)
+
+
+@pytest.mark.parametrize("np_req", [1, 3])
+def test_latent_graph_replay_matches_eager(np_req):
+    """The latent call (and, when split, its combine) captured once and
+    replayed with new queries and new entry lists written between replays."""
+    from block_sparse_attention_indexer_amd import latent_inputs as LI
+    print(f"[case] latent graph np={np_req}", flush=True)
+    wl = LI.LatentWorkload("g_latent", new_lens=(1, 3, 2), swa_cache_lens=(900, 4000, 130),
+                           comp_lens=(600, 1500, 40), num_heads=64, window=96, top_c=200,
+                           sink_mean=1.0, bad_frac=0.05, seed=23)
+    inp = LI.make_latent_inputs(wl, DEV)
+    swa, comp = B.latent_leaves_of_inputs(inp)
+    np_ = B.msa_latent_partitions(wl.batch, wl.max_seq_length, wl.num_heads, 1, wl.window,
+                                  wl.top_c, np_req)
+    ws = torch.empty(max(1, B.msa_latent_workspace_bytes(wl.batch, wl.max_seq_length, wl.num_heads,
+                                                         1, wl.window, wl.top_c, np_)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty((wl.total_rows, wl.num_heads, 128), dtype=torch.bfloat16, device=DEV)
+
+    def step(out_buf):
+        B.msa_latent_attention_paged(out_buf, inp.q, inp.input_row_offsets, wl.batch,
+                                     wl.max_seq_length, inp.comp_indices, inp.attn_sink, swa, comp,
+                                     wl.num_heads, 1, wl.window, wl.softmax_scale, np_, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    out_e = torch.empty_like(out)
+    offs = inp.input_row_offsets.cpu().tolist()
+    for rep in range(3):
+        inp.q.copy_(torch.randn(inp.q.shape, generator=gen, device=DEV).to(inp.q.dtype))
+        # new lists: valid entries of each sequence's compressed leaf, some -1
+        for b in range(wl.batch):
+            n = wl.comp_lens[b]
+            rows = offs[b + 1] - offs[b]
+            lst = torch.randint(-1, max(n, 1), (rows, 1, wl.top_c), generator=gen, device=DEV)
+            inp.comp_indices[offs[b]:offs[b + 1]] = lst.to(torch.int32)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        out_g = out.clone()
+        step(out_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_g.float()).all(), f"replay {rep}"
+        assert torch.equal(out_g, out_e), f"replay {rep}: graph output differs from eager"
