@@ -25,10 +25,10 @@ split-K combine when the row is split), measured live with HIP events on the
 launch stream over K back-to-back calls; achieved = algorithmic bytes (or
 flops) of one call / that duration.
 
-Latent workload (--workload latent_decode): one step is one
-msa_latent_attention_paged call; the metric is the latent bytes it must
-gather (window positions and valid listed entries, 256 bytes each) per
-second.  The steps rotate over input sets of the same shape with different
+Latent workloads (--workload latent_decode, latent_decode_fp8): one step is
+one msa_latent_attention_paged call; the metric is the latent bytes it must
+gather (window positions and valid listed entries, 256 bytes each in BF16,
+128 in FP8) per second.  The steps rotate over input sets of the same shape with different
 data, so that the data of consecutive steps does not stay in the GPU's
 last-level cache.
 
@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--workload", default="decode_batch64",
                     help="decode_small | decode_batch64 | spec_decode | prefill_ragged | "
                          "decode_fp8_long | decode_fp8_long_fp8ik | spec_decode_reuse | "
-                         "latent_decode | all")
+                         "latent_decode | latent_decode_fp8 | all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
@@ -121,21 +121,25 @@ def algorithmic_work(wl, d_idx, rows=None):
 def latent_work(inp):
     """Latent bytes one call must gather: for every row and latent head, its
     window positions plus its listed entries inside the compressed leaf (each
-    occurrence), 256 bytes each (one BF16 vector of 128); and flops, 4 * 128
-    per (query head, entry)."""
+    occurrence), 256 bytes each for a BF16 leaf and 128 for an FP8 e4m3 leaf
+    (one vector of 128); and flops, 4 * 128 per (query head, entry)."""
     wl = inp.wl
     offs = inp.input_row_offsets.cpu().numpy()
     swa_c = inp.swa_cache_lengths.cpu().numpy()
     comp_c = inp.comp_cache_lengths.cpu().numpy()
     lists = inp.comp_indices.cpu().numpy()
-    ent = 0
+    ent = nbytes = 0
+    esz = {"bf16": 2, "fp8_e4m3": 1}
     for b in range(wl.batch):
         for r in range(offs[b], offs[b + 1]):
             p = int(swa_c[b]) + (r - offs[b])
             n_swa = min(wl.window, p + 1) if wl.window > 0 else 0
             lst = lists[r]
-            ent += wl.num_latent_heads * n_swa + int(((lst >= 0) & (lst < comp_c[b])).sum())
-    return {"entries": ent, "latent_bytes": ent * 256,
+            n_comp = int(((lst >= 0) & (lst < comp_c[b])).sum())
+            ent += wl.num_latent_heads * n_swa + n_comp
+            nbytes += 128 * (wl.num_latent_heads * n_swa * esz[wl.swa_dtype] +
+                             n_comp * esz[wl.comp_dtype])
+    return {"entries": ent, "latent_bytes": nbytes,
             "flops": ent * 4 * 128 * (wl.num_heads // wl.num_latent_heads)}
 
 
@@ -583,6 +587,7 @@ def latent_cpu_baseline(inp, seconds):
     except Exception:  # pragma: no cover - reporting only
         threads = 1
     wl = inp.wl
+    esz = {"bf16": 2, "fp8_e4m3": 1}
     offs = inp.input_row_offsets.cpu().numpy()
     probs = []
     for b in range(wl.batch):
@@ -590,7 +595,8 @@ def latent_cpu_baseline(inp, seconds):
         nb = 0
         for r in range(len(orig)):
             bb, _, p = LO.row_position(pb, r)
-            nb += 256 * sum(len(LO.window_positions(p, pb.window)) + len(LO.listed_entries(pb, r, hl, bb))
+            nb += 128 * sum(esz[wl.swa_dtype] * len(LO.window_positions(p, pb.window)) +
+                            esz[wl.comp_dtype] * len(LO.listed_entries(pb, r, hl, bb))
                             for hl in range(pb.num_latent_heads))
         probs.append((pb, len(orig), nb))
     spent, nbytes, rows, passes = 0.0, 0, 0, 0
@@ -625,7 +631,7 @@ def main():
         write_traffic_record(args)
         return
     names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long",
-              "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode"]
+              "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode", "latent_decode_fp8"]
              if args.workload == "all" else [args.workload])
     for name in names:
         res = run_latent(name, args) if is_latent(name) else run(name, args)

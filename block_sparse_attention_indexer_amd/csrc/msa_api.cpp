@@ -419,10 +419,11 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
     if (!comp || !comp_indices) return MSA_ERR_NULL;
     if ((st = check_latent_leaf(comp, num_latent_heads, comp->max_cache_length)) != MSA_OK) return st;
   }
-  // the kernel's tile format is BF16
-  if ((window > 0 && swa->cache.dtype != MSA_DTYPE_BF16) ||
-      (top_c > 0 && comp->cache.dtype != MSA_DTYPE_BF16))
-    return MSA_ERR_DTYPE;
+  // one tile format per call: the leaves that are read share their type
+  const int leaf_dtype = window > 0 ? swa->cache.dtype
+                         : top_c > 0 ? comp->cache.dtype
+                                     : (int)MSA_DTYPE_BF16;
+  if (window > 0 && top_c > 0 && comp->cache.dtype != swa->cache.dtype) return MSA_ERR_DTYPE;
   int cus = 0;
   if (num_partitions == 0 && (st = current_device(&cus)) != MSA_OK) return st;
   const int np = plan_latent(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
@@ -446,6 +447,7 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
   p.sink = attn_sink;
   if (window > 0) p.swa = leaf_of(swa);
   if (top_c > 0) p.comp = leaf_of(comp);
+  p.fp8 = leaf_dtype == MSA_DTYPE_FP8_E4M3;
   p.H = num_heads;
   p.H_lat = num_latent_heads;
   p.G = num_heads / num_latent_heads;

@@ -21,7 +21,8 @@ struct LatentParams {
   const int32_t* lists;   // [R][H_lat][top_c] compressed-leaf entries
   int32_t top_c;
   const float* sink;      // [H]
-  LatentLeaf swa, comp;    // BF16 leaves
+  LatentLeaf swa, comp;
+  int32_t fp8;            // 1: both leaves FP8 e4m3 (scale-free), 0: both BF16
   int32_t H, H_lat, G;    // query heads, latent heads, query heads per latent head
   int32_t ncg;            // column groups of 64 query heads per latent head
   int32_t window, np, rcap;

@@ -20,16 +20,20 @@
 // per column tile.  At the end the four waves' softmax states are merged
 // through LDS.
 //
-// The tile is stored row-major, 256 bytes per entry, with 16-byte column c
-// of row pos at c ^ f(pos), f(pos) = ((pos & 7) << 1) | ((pos >> 3) & 1),
-// which keeps the transposing value reads free of LDS bank conflicts (the
-// 16-byte key reads measure 2-way conflicted with it).
+// The tile is stored row-major, one row per entry: BF16 leaves 256 bytes,
+// 16-byte column c of row pos at c ^ f(pos), f(pos) = ((pos & 7) << 1) |
+// ((pos >> 3) & 1), which keeps the transposing value reads free of LDS
+// bank conflicts (the 16-byte key reads measure 2-way conflicted with it);
+// FP8 e4m3 leaves 128 bytes, column c at c ^ fp8_vswz(pos), the codes being
+// widened to BF16 (exactly) as the MFMA operands are read.
 //
 // Entries a partition does not attend (a list value outside [0, leaf
 // length), the padding after the row's last entry) are still fetched -- from
-// the row's own query vector, a finite stand-in -- so that every wave issues
-// the same number of DMAs per tile and the vmcnt waits stay exact; their
-// scores are masked to -inf, so their probability is exactly 0.
+// the row's own query vector -- so that every wave issues the same number of
+// DMAs per tile and the vmcnt waits stay exact; their scores are masked to
+// -inf, so their probability is exactly 0.  For BF16 leaves those stand-in
+// bytes are finite; for FP8 leaves they could decode as NaN, so the wave
+// zeroes such rows of its tile before reading it.
 //
 // The sink joins one wave's running softmax in partition 0 as one more
 // logit with no value (max = sink, sum = 1 before any entry), so neither the
@@ -44,15 +48,13 @@
 namespace msa {
 
 constexpr int kLatWaves = 4;
-constexpr int kLatRowBytes = 256;                              // one BF16 latent vector
-constexpr int kLatTileBytes = kLatentTile * kLatRowBytes;      // 8 KiB
 constexpr int kLatStages = 4;                                  // per wave
-constexpr int kLatDma = kLatTileBytes / 1024;                  // DMAs per tile: 8
+constexpr int kLatRingBytes = kLatStages * kLatentTile * 256;  // per wave: 32 KiB
 constexpr float kLatLazy = 8.f;   // log2 headroom before the running max moves
 
 struct LatentLds {
   // per-wave tile rings; after the loop, each wave's merged-state area
-  char ring[kLatWaves][kLatStages * kLatTileBytes];
+  char ring[kLatWaves][kLatRingBytes];
   // first byte of each entry's latent vector, or null: not attended; after
   // the loop, the waves' per-column max and sum
   const char* src[kLatentMaxSlots];
@@ -60,8 +62,14 @@ struct LatentLds {
 
 __device__ __forceinline__ int lat_swz(int pos) { return ((pos & 7) << 1) | ((pos >> 3) & 1); }
 
-template <int NCT>
+template <int NCT, bool FP8>
 __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentParams p) {
+  constexpr int RB = FP8 ? 128 : 256;                 // bytes per entry row
+  constexpr int ESZ = FP8 ? 1 : 2;                    // bytes per element
+  constexpr int kTileBytes = kLatentTile * RB;
+  constexpr int kDma = kTileBytes / 1024;             // DMAs per tile: 8 (BF16), 4 (FP8)
+  constexpr int kLanesPerRow = RB / 16;
+  constexpr int kRowsPerDma = 64 / kLanesPerRow;
   __shared__ __attribute__((aligned(16))) LatentLds L;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform((int)(tid >> 6));
@@ -92,9 +100,13 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     const int hcol = cg * 64 + 16 * ct + l16;
     col_ok[ct] = hcol < p.G;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qf[ct][s] = col_ok[ct] ? ld16(qrow + (size_t)(hl * p.G + hcol) * kDim + 32 * s + 8 * g)
+    for (int s = 0; s < 4; ++s) {
+      // contraction dims of k-step s for lane group g: BF16 32s + 8g + j;
+      // FP8 (a lane's 16 key bytes cover two k-steps) 16g + 64(s/2) + 8(s%2) + j
+      const int d0 = FP8 ? 16 * g + 64 * (s >> 1) + 8 * (s & 1) : 32 * s + 8 * g;
+      qf[ct][s] = col_ok[ct] ? ld16(qrow + (size_t)(hl * p.G + hcol) * kDim + d0)
                              : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   // ---- this partition's entries ---------------------------------------------
@@ -120,8 +132,8 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     const int32_t* comp_tab = p.comp.table + (size_t)b * p.comp.stride;
     const char* swa_base = static_cast<const char*>(p.swa.pool.data);
     const char* comp_base = static_cast<const char*>(p.comp.pool.data);
-    if (swa_base) swa_base += (size_t)hl * p.swa.pool.head_stride * 2;
-    if (comp_base) comp_base += (size_t)hl * p.comp.pool.head_stride * 2;
+    if (swa_base) swa_base += (size_t)hl * p.swa.pool.head_stride * ESZ;
+    if (comp_base) comp_base += (size_t)hl * p.comp.pool.head_stride * ESZ;
     int ent[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -149,10 +161,10 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
       if (i < ntile * kLatentTile) {
         const char* a = nullptr;
         if (pg[k] >= 0)
-          a = s < n_swa ? swa_base + (size_t)pg[k] * p.swa.pool.page_stride * 2 +
-                              (size_t)(ent[k] & 127) * p.swa.pool.token_stride * 2
-                        : comp_base + (size_t)pg[k] * p.comp.pool.page_stride * 2 +
-                              (size_t)(ent[k] & 127) * p.comp.pool.token_stride * 2;
+          a = s < n_swa ? swa_base + (size_t)pg[k] * p.swa.pool.page_stride * ESZ +
+                              (size_t)(ent[k] & 127) * p.swa.pool.token_stride * ESZ
+                        : comp_base + (size_t)pg[k] * p.comp.pool.page_stride * ESZ +
+                              (size_t)(ent[k] & 127) * p.comp.pool.token_stride * ESZ;
         L.src[i] = a;
       }
     }
@@ -181,34 +193,51 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   __syncthreads();
 
   // ---- this wave's tiles ----------------------------------------------------------
-  // DMA i of a tile fetches rows 4i .. 4i + 3; lane (l16, g) lands in row
-  // 4i + g at physical column l16, which holds logical column l16 ^ f(row).
-  // Rows that are not attended fetch 16 bytes of the row's first query
-  // vector instead.
+  // DMA i of a tile fetches rows kRowsPerDma * i onwards; lane L lands in row
+  // kRowsPerDma * i + L / kLanesPerRow at physical column L % kLanesPerRow,
+  // which holds logical column (L % kLanesPerRow) ^ swizzle(row).  Rows that
+  // are not attended fetch 16 bytes of the row's first query vector instead.
+  auto swz = [](int pos) { return FP8 ? fp8_vswz(pos) : lat_swz(pos); };
   char* ring = L.ring[wave];
   const int my_n = ntile > wave ? (ntile - wave + kLatWaves - 1) / kLatWaves : 0;
   const char* dummy = reinterpret_cast<const char*>(qrow) + 16 * l16;
-  uint32_t colb[kLatDma];
+  const int drow = lane / kLanesPerRow, dcol = lane % kLanesPerRow;
+  uint32_t colb[kDma];
 #pragma unroll
-  for (int i = 0; i < kLatDma; ++i) colb[i] = (uint32_t)((l16 ^ lat_swz(4 * i + g)) << 4);
+  for (int i = 0; i < kDma; ++i) colb[i] = (uint32_t)((dcol ^ swz(kRowsPerDma * i + drow)) << 4);
   auto issue = [&](int j) {
     const int tb = (wave + kLatWaves * j) * kLatentTile;
-    char* stage = ring + (j % kLatStages) * kLatTileBytes;
-    const char* a[kLatDma];
+    char* stage = ring + (j % kLatStages) * kTileBytes;
+    const char* a[kDma];
 #pragma unroll
-    for (int i = 0; i < kLatDma; ++i) a[i] = L.src[tb + 4 * i + g];
+    for (int i = 0; i < kDma; ++i) a[i] = L.src[tb + kRowsPerDma * i + drow];
 #pragma unroll
-    for (int i = 0; i < kLatDma; ++i) dma16(a[i] ? a[i] + colb[i] : dummy, stage + 4 * i * kLatRowBytes);
+    for (int i = 0; i < kDma; ++i) dma16(a[i] ? a[i] + colb[i] : dummy, stage + kRowsPerDma * i * RB);
   };
 
-  // lane-constant LDS offsets.  K A-operand: row 16pt + l16, logical column
-  // 4s + g.  X^T A-operand (transposing read h, dim tile dt): source lane
-  // (l16, g) reads row 16h + 4g + l16 / 4 at dims 16dt + 4(l16 % 4), so
-  // output lane (m, g) receives dim 16dt + m of rows 16h + 4g + k -- the
-  // P^T B-operand layout.
-  const int kq = l16 * kLatRowBytes + ((g ^ lat_swz(l16)) << 4);
-  const int vrow = 4 * g + (l16 >> 2);
-  const int vq = vrow * kLatRowBytes + ((((l16 & 3) >> 1) ^ lat_swz(vrow)) << 4) + 8 * (l16 & 1);
+  // lane-constant LDS offsets.
+  // BF16 K A-operand: row 16pt + l16, logical column 4s + g.
+  // FP8 K A-operands: row 16pt + l16, logical column g + 4h holds the 16
+  //   bytes of k-steps 2h and 2h + 1.
+  // BF16 X^T A-operand (transposing read h, dim tile dt): source lane (l16,
+  //   g) reads row 16h + 4g + l16 / 4 at dims 16dt + 4(l16 % 4), so output
+  //   lane (m, g) receives dim 16dt + m of rows 16h + 4g + k -- the P^T
+  //   B-operand layout.
+  // FP8 X^T A-operand (one 8-bit transposing read, dim tile dt): source lane
+  //   l16 reads the row of position k = l16 / 2, 16(k / 4) + 4g + k % 4, at
+  //   dims 16dt + 8(l16 % 2); within a 16-lane group output lane i, element
+  //   k is byte i % 8 of source lane i / 8 + 2k, so lane (m, g) receives dim
+  //   16dt + m of the same eight rows as the BF16 reads.
+  const int kq = FP8 ? l16 * RB : l16 * RB + ((g ^ lat_swz(l16)) << 4);
+  int vq;
+  if constexpr (FP8) {
+    const int k = l16 >> 1;
+    const int vr8 = 16 * (k >> 2) + 4 * g + (k & 3);
+    vq = vr8 * RB + (fp8_vswz(vr8) << 4) + 8 * (l16 & 1);
+  } else {
+    const int vrow = 4 * g + (l16 >> 2);
+    vq = vrow * RB + ((((l16 & 3) >> 1) ^ lat_swz(vrow)) << 4) + 8 * (l16 & 1);
+  }
 
 #pragma unroll
   for (int j = 0; j < kLatStages - 1; ++j)
@@ -218,13 +247,28 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     // this wave's DMAs of tile j are done once at most those of the younger
     // tiles in flight remain (the wave reads only what it fetched itself)
     const int younger = min(my_n - 1 - j, kLatStages - 2);
-    if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLatDma));
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLatDma));
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDma));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     // the stage of tile j - 1 is free: this wave's reads of it have returned
     if (j + kLatStages - 1 < my_n) issue(j + kLatStages - 1);
 
-    const char* tile = ring + (j % kLatStages) * kLatTileBytes;
+    char* tile = ring + (j % kLatStages) * kTileBytes;
+    const int tb = (wave + kLatWaves * j) * kLatentTile;
+    const uint32_t live = (uint32_t)ballot(lane < kLatentTile && L.src[tb + (lane & 31)] != nullptr);
+    if constexpr (FP8) {
+      // rows that are not attended hold stand-in bytes: zero them (this
+      // wave's own DMAs of the tile have landed; its LDS operations run in
+      // order, so the reads below see the zeros)
+      if (live != 0xFFFFFFFFu) {
+#pragma unroll
+        for (int k = 0; k < kTileBytes / 16 / 64; ++k) {
+          const int idx = lane + 64 * k;
+          if (!((live >> (idx / kLanesPerRow)) & 1u))
+            *reinterpret_cast<u32x4*>(tile + idx * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
     // The key operands are requested together (one LDS latency per tile);
     // the transposed value reads are issued right behind the score MFMAs, so
     // they land while the scores and the softmax run.  (LDS results return
@@ -232,12 +276,22 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     // values first would make the first MFMA wait for them.)
     u32x4 ka[2][4];
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
+    for (int pt = 0; pt < 2; ++pt) {
+      if constexpr (FP8) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        ka[pt][s] = *reinterpret_cast<const u32x4*>(tile + 16 * pt * kLatRowBytes + (kq ^ (s << 6)));
-    const int tb = (wave + kLatWaves * j) * kLatentTile;
-    const uint32_t live = (uint32_t)ballot(lane < kLatentTile && L.src[tb + (lane & 31)] != nullptr);
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * pt + l16;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(tile + kq + 16 * pt * RB +
+                                                          (((g + 4 * h) ^ fp8_vswz(row)) << 4));
+          ka[pt][2 * h] = fp8x8_to_bf16x8(u32x2{w.x, w.y});
+          ka[pt][2 * h + 1] = fp8x8_to_bf16x8(u32x2{w.z, w.w});
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          ka[pt][s] = *reinterpret_cast<const u32x4*>(tile + 16 * pt * RB + (kq ^ (s << 6)));
+      }
+    }
     // this lane's rows of the tile are 16pt + 4g + i: bit 4pt + i of m8
     const uint32_t lg = live >> (4 * g);
     const uint32_t m8 = (lg & 0xFu) | ((lg >> 12) & 0xF0u);
@@ -255,9 +309,13 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     u32x2 va[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const char* base = tile + (vq ^ (dt << 5));
-      va[dt][0] = lds_tr_b16(base);
-      va[dt][1] = lds_tr_b16(base + 16 * kLatRowBytes);
+      if constexpr (FP8) {
+        va[dt][0] = lds_tr_b8(tile + (vq ^ (dt << 4)));
+      } else {
+        const char* base = tile + (vq ^ (dt << 5));
+        va[dt][0] = lds_tr_b16(base);
+        va[dt][1] = lds_tr_b16(base + 16 * RB);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -310,7 +368,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
                      pack_bf16(S[1][ct][0], S[1][ct][1]), pack_bf16(S[1][ct][2], S[1][ct][3])};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const u32x4 a = {va[dt][0].x, va[dt][0].y, va[dt][1].x, va[dt][1].y};
+      const u32x4 a = FP8 ? fp8x8_to_bf16x8(va[dt][0]) : u32x4{va[dt][0].x, va[dt][0].y, va[dt][1].x, va[dt][1].y};
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = mfma_bf16(a, bp[ct], O[dt][ct]);
     }
@@ -376,13 +434,19 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   }
 }
 
+template <bool FP8>
+static void launch_latent_t(const LatentParams& p, dim3 grid, dim3 block, hipStream_t s) {
+  const int cols = std::min(64, p.G);   // heads of the widest column group
+  if (cols <= 16) hipLaunchKernelGGL((latent_attn_kernel<1, FP8>), grid, block, 0, s, p);
+  else if (cols <= 32) hipLaunchKernelGGL((latent_attn_kernel<2, FP8>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((latent_attn_kernel<4, FP8>), grid, block, 0, s, p);
+}
+
 hipError_t launch_latent(const LatentParams& p, hipStream_t s) {
   const size_t nwg = (size_t)p.batch * p.max_seq * p.H_lat * p.ncg * p.np;
-  const int cols = std::min(64, p.G - 0);   // heads of the widest column group
   const dim3 grid((unsigned)nwg), block(64 * kLatWaves);
-  if (cols <= 16) hipLaunchKernelGGL(latent_attn_kernel<1>, grid, block, 0, s, p);
-  else if (cols <= 32) hipLaunchKernelGGL(latent_attn_kernel<2>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(latent_attn_kernel<4>, grid, block, 0, s, p);
+  if (p.fp8) launch_latent_t<true>(p, grid, block, s);
+  else launch_latent_t<false>(p, grid, block, s);
   return hipGetLastError();
 }
 

@@ -49,4 +49,12 @@ __device__ __forceinline__ u32x2 lds_tr_b8(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Column swizzle of FP8 tiles (128-byte rows of e4m3): 16-byte column c of
+// row pos is stored at c ^ fp8_vswz(pos), built from bits 1, 4 and 2 of pos,
+// which keeps the rows of a transposing 8-bit read (ds_read_b64_tr_b8) in
+// distinct bank groups.
+__device__ __forceinline__ int fp8_vswz(int pos) {
+  return ((pos >> 1) & 1) | (((pos >> 4) & 1) << 1) | (((pos >> 2) & 1) << 2);
+}
+
 }  // namespace msa

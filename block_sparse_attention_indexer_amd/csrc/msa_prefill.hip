@@ -462,10 +462,6 @@ struct PrefillLds3 {
   uint32_t ring_msk[2 * kRingHalf];
 };
 
-// FP8 tile swizzles (16-byte column XOR masks of row pos)
-__device__ __forceinline__ int fp8_vswz(int pos) {
-  return ((pos >> 1) & 1) | (((pos >> 4) & 1) << 1) | (((pos >> 2) & 1) << 2);
-}
 
 template <bool FP8, int NCT>
 __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L) {

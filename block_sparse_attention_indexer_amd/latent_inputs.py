@@ -122,7 +122,15 @@ def latent_decode(seed: int = 0, batch: int = 64, heads: int = 64, window: int =
         top_c=top_c, sink_mean=2.0, seed=seed)
 
 
-LATENT_WORKLOADS = {"latent_decode": latent_decode}
+def latent_decode_fp8(seed: int = 0, **kw) -> LatentWorkload:
+    """latent_decode with both leaves stored as FP8 e4m3 (half the bytes per
+    latent vector)."""
+    w = latent_decode(seed, **kw)
+    return replace(w, name=w.name.replace("latent_decode", "latent_decode_fp8"),
+                   swa_dtype="fp8_e4m3", comp_dtype="fp8_e4m3")
+
+
+LATENT_WORKLOADS = {"latent_decode": latent_decode, "latent_decode_fp8": latent_decode_fp8}
 
 
 @dataclass

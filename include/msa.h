@@ -350,6 +350,9 @@ size_t msa_latent_workspace_bytes(int32_t batch, int32_t max_seq_length, int32_t
  * attn_sink         device float32 [num_heads].
  * swa, comp         the two leaves (num_heads == num_latent_heads in both);
  *                   swa may be NULL when window == 0, comp when top_c == 0.
+ *                   The leaves a call reads share one storage type (both
+ *                   BF16 or both FP8 e4m3), else MSA_ERR_DTYPE; FP8 codes
+ *                   are widened to BF16 exactly.
  *                   swa->lookup_stride must cover positions up to
  *                   swa->max_cache_length + max_seq_length - 1, and
  *                   comp->lookup_stride entries up to comp->max_cache_length - 1.

@@ -196,7 +196,13 @@ def test_latent_validation():
     assert latent(s, c, scale=0.0) == PARAM
     assert latent(s, c, scale=float("nan")) == PARAM
     assert latent(leaf(dtype=7), c) == DTYPE
-    assert latent(s, leaf(dtype=B.MSA_DTYPE_FP8_E4M3)) == DTYPE   # FP8 leaves not built
+    f8 = leaf(dtype=B.MSA_DTYPE_FP8_E4M3)
+    assert latent(s, f8) == DTYPE                              # leaves of two types
+    assert latent(f8, c) == DTYPE
+    # both FP8, or one FP8 leaf with the other not read: passes the type check
+    assert latent(f8, leaf(dtype=B.MSA_DTYPE_FP8_E4M3), ws=0) == NULL
+    assert latent(f8, None, top_c=0, lists=None, np_=1, ws=0) not in (NULL, SHAPE, PARAM, DTYPE)
+    assert latent(None, f8, window=0, ws=0) == NULL
     need = B.msa_latent_workspace_bytes(2, 1, 64, 1, 128, 512, 2)
     assert need >= 2 * 2 * 64 * 129 * 4
     assert latent(s, c, ws=need - 1) == WORKSPACE

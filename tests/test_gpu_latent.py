@@ -41,7 +41,7 @@ def check(wl, num_partitions=0, seqs=None, rows_per_seq=None):
     ref = L.latent_attention(pb, local)
     got = out[torch.tensor(rows, device=DEV, dtype=torch.long)]
     assert torch.isfinite(got.float()).all(), "non-finite output"
-    err = parity.check_attention(got, ref, "bf16", wl.name)
+    err = parity.check_attention(got, ref, wl.comp_dtype if wl.top_c else wl.swa_dtype, wl.name)
     say(f"  rows={len(rows)} max|err|={err:.3e}")
     return inp, out
 
@@ -133,3 +133,39 @@ def test_page_placement_gives_identical_results():
     b = B.run_latent(inp, num_partitions=2)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+FP8 = dict(swa_dtype="fp8_e4m3", comp_dtype="fp8_e4m3")
+
+
+@pytest.mark.parametrize("np_", [0, 3])
+def test_fp8_leaves_decode(np_):
+    # invalid and repeated list values leave rows of a tile unattended (their
+    # stand-in bytes must not reach the result); 64 heads on one latent head
+    check(wl("lat_fp8", [1] * 5, [300, 40, 5000, 127, 20000], [900, 10, 1300, 0, 6000], H=64,
+             window=128, top_c=600, sink_mean=1.5, bad_frac=0.1, dup_frac=0.05, seed=21, **FP8),
+          num_partitions=np_)
+
+
+def test_fp8_leaves_heads_and_rows():
+    # 3 latent heads of 16 query heads, multi-token rows; 40 query heads
+    # (a partial column tile) on a second case
+    check(wl("lat_fp8_hlat", [1, 4, 2], [1000, 200, 50], [400, 700, 31], H=48, H_lat=3, window=48,
+             top_c=96, sink_neg_inf_frac=0.3, bad_frac=0.1, seed=22, **FP8))
+    check(wl("lat_fp8_g40", [1, 1], [3000, 77], [800, 90], H=40, window=100, top_c=200, seed=23,
+             **FP8))
+
+
+def test_fp8_window_only_and_list_only():
+    check(wl("lat_fp8_win", [1, 2], [900, 30], [0, 0], H=16, window=200, top_c=0, seed=24, **FP8))
+    check(wl("lat_fp8_list", [1, 3], [900, 30], [500, 700], H=16, window=0, top_c=150, seed=25,
+             **FP8))
+
+
+def test_fp8_prefill_rows():
+    check(wl("lat_fp8_prefill", [300, 45], [0, 512], [300, 128], H=16, window=128, top_c=64,
+             seed=26, **FP8), rows_per_seq=40)
+
+
+def test_fp8_latent_decode_workload_sampled():
+    check(LI.latent_decode_fp8(), seqs=[0, 21, 42, 63])
