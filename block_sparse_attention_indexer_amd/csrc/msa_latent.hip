@@ -11,7 +11,8 @@
 // its entries to the address of its latent vector (in LDS).  The waves then
 // take the partition's tiles in turn (wave w: tiles w, w + 4, ...), each
 // streaming its own tiles through its own ring of LDS stages with
-// global->LDS DMA, three tiles in flight, so no wave waits for another
+// global->LDS DMA, a whole ring of tiles in flight (four BF16 tiles, eight
+// FP8 ones), so no wave waits for another
 // inside the loop.  A wave holds all of the group's query heads as MFMA
 // columns (up to four 16-column tiles): S^T = X . Q^T over a tile (X the
 // 32 latent rows), an online softmax over the rows, then O^T += X^T . P^T
@@ -48,8 +49,7 @@
 namespace msa {
 
 constexpr int kLatWaves = 4;
-constexpr int kLatStages = 4;                                  // per wave
-constexpr int kLatRingBytes = kLatStages * kLatentTile * 256;  // per wave: 32 KiB
+constexpr int kLatRingBytes = 4 * kLatentTile * 256;           // per wave: 32 KiB
 constexpr float kLatLazy = 8.f;   // log2 headroom before the running max moves
 
 struct LatentLds {
@@ -62,6 +62,50 @@ struct LatentLds {
 
 __device__ __forceinline__ int lat_swz(int pos) { return ((pos & 7) << 1) | ((pos >> 3) & 1); }
 
+// o *= s in place in the accumulation registers.  The accumulators live in
+// AGPRs (they are MFMA results and operands); written as plain C++, the
+// multiply makes the compiler copy every accumulator to VGPRs at the top of
+// each tile, whether or not the (rare) rescale runs.  The last MFMA that
+// wrote o is a whole score phase earlier; the trailing s_nop covers the
+// AGPR-write -> MFMA-read wait states of the next accumulation.
+__device__ __forceinline__ void scale_acc(f32x4& o, float s) {
+  float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
+  float t0, t1, t2, t3;
+  __asm__ volatile(
+      "v_accvgpr_read_b32 %4, %0\n\t"
+      "v_accvgpr_read_b32 %5, %1\n\t"
+      "v_accvgpr_read_b32 %6, %2\n\t"
+      "v_accvgpr_read_b32 %7, %3\n\t"
+      "v_mul_f32 %4, %8, %4\n\t"
+      "v_mul_f32 %5, %8, %5\n\t"
+      "v_mul_f32 %6, %8, %6\n\t"
+      "v_mul_f32 %7, %8, %7\n\t"
+      "v_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_write_b32 %1, %5\n\t"
+      "v_accvgpr_write_b32 %2, %6\n\t"
+      "v_accvgpr_write_b32 %3, %7\n\t"
+      "s_nop 4"
+      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "v"(s));
+  o = f32x4{x0, x1, x2, x3};
+}
+
+// Wait until at most n tiles of kDma DMAs each are still in flight (the
+// count must be an immediate, hence the cases).
+template <int kDma>
+__device__ __forceinline__ void wait_tiles(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDma)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kDma)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * kDma)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * kDma)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * kDma)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * kDma)); break;
+  }
+}
+
 template <int NCT, bool FP8>
 __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentParams p) {
   constexpr int RB = FP8 ? 128 : 256;                 // bytes per entry row
@@ -70,6 +114,8 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   constexpr int kDma = kTileBytes / 1024;             // DMAs per tile: 8 (BF16), 4 (FP8)
   constexpr int kLanesPerRow = RB / 16;
   constexpr int kRowsPerDma = 64 / kLanesPerRow;
+  constexpr int kStages = kLatRingBytes / kTileBytes;  // tiles in flight per wave: 4, 8
+  static_assert(kStages <= 8 && kStages * kDma <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) LatentLds L;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform((int)(tid >> 6));
@@ -207,7 +253,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   for (int i = 0; i < kDma; ++i) colb[i] = (uint32_t)((dcol ^ swz(kRowsPerDma * i + drow)) << 4);
   auto issue = [&](int j) {
     const int tb = (wave + kLatWaves * j) * kLatentTile;
-    char* stage = ring + (j % kLatStages) * kTileBytes;
+    char* stage = ring + (j % kStages) * kTileBytes;
     const char* a[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) a[i] = L.src[tb + kRowsPerDma * i + drow];
@@ -240,20 +286,15 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   }
 
 #pragma unroll
-  for (int j = 0; j < kLatStages - 1; ++j)
+  for (int j = 0; j < kStages; ++j)
     if (j < my_n) issue(j);
 
   for (int j = 0; j < my_n; ++j) {
     // this wave's DMAs of tile j are done once at most those of the younger
     // tiles in flight remain (the wave reads only what it fetched itself)
-    const int younger = min(my_n - 1 - j, kLatStages - 2);
-    if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDma));
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // the stage of tile j - 1 is free: this wave's reads of it have returned
-    if (j + kLatStages - 1 < my_n) issue(j + kLatStages - 1);
+    wait_tiles<kDma>(min(my_n - 1 - j, kStages - 1));
 
-    char* tile = ring + (j % kLatStages) * kTileBytes;
+    char* tile = ring + (j % kStages) * kTileBytes;
     const int tb = (wave + kLatWaves * j) * kLatentTile;
     const uint32_t live = (uint32_t)ballot(lane < kLatentTile && L.src[tb + (lane & 31)] != nullptr);
     if constexpr (FP8) {
@@ -355,11 +396,13 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
       l_run[ct] = l_run[ct] * alpha[ct] + lsum;
       m_run[ct] = m_new;
     }
-    if (__builtin_amdgcn_ballot_w64(any_move)) {
+    // O is still zero on the wave's first tile; later moves are rare (the
+    // lazy threshold)
+    if (j > 0 && __builtin_amdgcn_ballot_w64(any_move)) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) O[dt][ct] *= alpha[ct];
+        for (int ct = 0; ct < NCT; ++ct) scale_acc(O[dt][ct], alpha[ct]);
     }
     u32x4 bp[NCT];
 #pragma unroll
@@ -371,6 +414,12 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
       const u32x4 a = FP8 ? fp8x8_to_bf16x8(va[dt][0]) : u32x4{va[dt][0].x, va[dt][0].y, va[dt][1].x, va[dt][1].y};
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) O[dt][ct] = mfma_bf16(a, bp[ct], O[dt][ct]);
+    }
+    // the stage of tile j is free once this wave's reads of it have
+    // returned (the MFMAs above consumed them)
+    if (j + kStages < my_n) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      issue(j + kStages);
     }
   }
 

@@ -169,3 +169,16 @@ def test_fp8_prefill_rows():
 
 def test_fp8_latent_decode_workload_sampled():
     check(LI.latent_decode_fp8(), seqs=[0, 21, 42, 63])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_running_max_moves_between_tiles(dtype):
+    # a softmax scale of 6/sqrt(128) spreads the scores by tens of units (the
+    # values stay of unit size, so the usual bar holds), so a wave's running
+    # maximum moves by more than its lazy threshold after its first tile and
+    # the accumulators are rescaled inside the loop (about a hundred times in
+    # this case)
+    check(wl(f"lat_moves_{dtype}", [1] * 4, [3000, 700, 9000, 100], [4000, 1500, 2500, 600], H=64,
+             window=128, top_c=1024, scale=6.0 / 128 ** 0.5, seed=27, swa_dtype=dtype,
+             comp_dtype=dtype),
+          num_partitions=1)
