@@ -58,6 +58,8 @@ struct LatentLds {
   // first byte of each entry's latent vector, or null: not attended; after
   // the loop, the waves' per-column max and sum
   const char* src[kLatentMaxSlots];
+  // the group's query vectors, [head][128] BF16 (read into registers once)
+  char q[64 * 256];
 };
 
 __device__ __forceinline__ int lat_swz(int pos) { return ((pos & 7) << 1) | ((pos >> 3) & 1); }
@@ -102,7 +104,8 @@ __device__ __forceinline__ void wait_tiles(int n) {
     case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * kDma)); break;
     case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * kDma)); break;
     case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * kDma)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * kDma)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * kDma)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * kDma)); break;
   }
 }
 
@@ -130,7 +133,14 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   id /= p.H_lat;
   const int b = id / p.max_seq, t = id % p.max_seq;
   // the sequence's lengths are read together with its row offsets (one
-  // memory round trip, not two)
+  // memory round trip, not two), and so are the sinks
+  bool col_ok[NCT];
+  float sink_v[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    col_ok[ct] = cg * 64 + 16 * ct + l16 < p.G;
+    sink_v[ct] = p.sink[hl * p.G + (col_ok[ct] ? cg * 64 + 16 * ct + l16 : 0)];
+  }
   const int r0 = p.offs[b], r1 = p.offs[b + 1];
   const int swa_len = p.window > 0 ? p.swa.clen[b] : 0;
   const int comp_len = p.top_c > 0 ? p.comp.clen[b] : 0;
@@ -138,22 +148,11 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   const int r = r0 + t;
 
   // ---- queries: the group's heads as NCT 16-column MFMA tiles -------------------
+  // They reach LDS by DMA right ahead of the first tiles and registers after
+  // that; loaded into registers here, they would sit on the path of the list
+  // and page-table loads (loads return in order).
   const uint16_t* qrow = p.q + (size_t)r * p.H * kDim;
   u32x4 qf[NCT][4];
-  bool col_ok[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int hcol = cg * 64 + 16 * ct + l16;
-    col_ok[ct] = hcol < p.G;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // contraction dims of k-step s for lane group g: BF16 32s + 8g + j;
-      // FP8 (a lane's 16 key bytes cover two k-steps) 16g + 64(s/2) + 8(s%2) + j
-      const int d0 = FP8 ? 16 * g + 64 * (s >> 1) + 8 * (s & 1) : 32 * s + 8 * g;
-      qf[ct][s] = col_ok[ct] ? ld16(qrow + (size_t)(hl * p.G + hcol) * kDim + d0)
-                             : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
 
   // ---- this partition's entries ---------------------------------------------
   const int pos = swa_len + t;
@@ -225,7 +224,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     m_run[ct] = neg_inf();
     l_run[ct] = 0.f;
     if (pi == 0 && wave == 0 && col_ok[ct]) {
-      const float sk = p.sink[hl * p.G + cg * 64 + 16 * ct + l16];
+      const float sk = sink_v[ct];
       if (sk != neg_inf()) {
         m_run[ct] = sk * kLog2e;
         l_run[ct] = g == 0 ? 1.f : 0.f;   // counted once per column
@@ -285,9 +284,34 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     vq = vrow * RB + ((((l16 & 3) >> 1) ^ lat_swz(vrow)) << 4) + 8 * (l16 & 1);
   }
 
+  // the queries: wave w < NCT fetches heads 16w .. 16w + 15 of the group
+  // (four per DMA; a head past the group fetches head 0's vector instead)
+  if (wave < NCT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hq = 16 * wave + 4 * i + (lane >> 4);
+      const int head = cg * 64 + hq < p.G ? hl * p.G + cg * 64 + hq : hl * p.G;
+      dma16(reinterpret_cast<const char*>(qrow + (size_t)head * kDim) + 16 * l16,
+            L.q + (16 * wave + 4 * i) * 256);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kStages; ++j)
     if (j < my_n) issue(j);
+  // the query DMAs are older than the tiles': they have landed once at most
+  // the tiles' remain; then every wave's are visible after the barrier
+  wait_tiles<kDma>(min(my_n, kStages));
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // contraction dims of k-step s for lane group g: BF16 32s + 8g + j;
+      // FP8 (a lane's 16 key bytes cover two k-steps) 16g + 64(s/2) + 8(s%2) + j
+      const int d0 = FP8 ? 16 * g + 64 * (s >> 1) + 8 * (s & 1) : 32 * s + 8 * g;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(L.q + (16 * ct + l16) * 256 + 2 * d0);
+      qf[ct][s] = col_ok[ct] ? v : u32x4{0u, 0u, 0u, 0u};
+    }
 
   for (int j = 0; j < my_n; ++j) {
     // this wave's DMAs of tile j are done once at most those of the younger
