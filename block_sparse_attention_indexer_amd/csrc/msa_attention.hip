@@ -356,6 +356,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int sub = threadIdx.x & 31;
   const size_t stride = (size_t)p.rcap * p.H_q;          // between partitions
   const size_t base = (size_t)r * p.H_q + hq;
+  const float* po = p.part_o + base * kDim + 4 * sub;
+  // the first eight partitions' outputs are requested together with the
+  // lse values (one memory round trip after the offsets, not two); a
+  // partition's weight is applied with a select, so a partial of weight 0
+  // never enters the sum
+  // (unconditional loads: a partition past np re-reads partition 0 and is
+  // masked below; under a branch the compiler would wait after each load)
+  f32x4 v0[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    v0[k] = *reinterpret_cast<const f32x4*>(po + (k < p.np ? k : 0) * stride * kDim);
   const float l0 = sub < p.np ? p.part_lse[sub * stride + base] : neg_inf();
   const float l1 = sub + 32 < p.np ? p.part_lse[(sub + 32) * stride + base] : neg_inf();
   float M = fmaxf(l0, l1);
@@ -367,20 +378,24 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) den += __shfl_xor(den, o, 32);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* po = p.part_o + base * kDim + 4 * sub;
-  for (int pi0 = 0; pi0 < p.np; pi0 += 8) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float w = __shfl(w0, k, 32);
+    if (k < p.np && w != 0.f) acc += w * v0[k];
+  }
+  for (int pi0 = 8; pi0 < p.np; pi0 += 8) {
     f32x4 v[8];
     float w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int pi = pi0 + k;
       w[k] = pi < 32 ? __shfl(w0, pi, 32) : __shfl(w1, pi - 32, 32);
-      v[k] = (pi < p.np && w[k] != 0.f) ? *reinterpret_cast<const f32x4*>(po + pi * stride * kDim)
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[k] = pi < p.np ? *reinterpret_cast<const f32x4*>(po + pi * stride * kDim)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (pi0 + k < p.np) acc += w[k] * v[k];
+      if (pi0 + k < p.np && w[k] != 0.f) acc += w[k] * v[k];
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const u32x2 o = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
