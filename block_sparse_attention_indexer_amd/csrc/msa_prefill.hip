@@ -821,10 +821,12 @@ __global__ __launch_bounds__(64 * kP3Waves) void attn_prefill3_kernel(AttnParams
 }
 
 void prefill_tiling(int G, bool /*fp8*/, int* tq, int* nct) {
-  // kP3Waves waves of at most 32 columns, both KV types
-  *tq = std::min(32, kP3Waves * 32 / G);
-  const int cpw = *tq * G / kP3Waves;
-  *nct = cpw > 16 ? 2 : 1;
+  // kP3Waves waves of at most 16 columns (one MFMA column tile), both KV
+  // types.  Two column tiles per wave do not fit the 128 VGPRs a wave of a
+  // 16-wave workgroup has: they spill inside the block loop (measured at
+  // group size 16: 32.6 ms against 11.3 ms with 16-token tiles).
+  *tq = std::min(32, kP3Waves * 16 / G);
+  *nct = 1;
 }
 
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s) {
@@ -839,13 +841,9 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s
   int tq, nct;
   prefill_tiling(p.G, fp8, &tq, &nct);
   const dim3 grid((unsigned)p.nwg), block(64 * kP3Waves);
-  if (fp8) {
-    if (nct == 2) hipLaunchKernelGGL((attn_prefill3_kernel<true, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill3_kernel<true, 1>), grid, block, 0, s, p);
-  } else {
-    if (nct == 2) hipLaunchKernelGGL((attn_prefill3_kernel<false, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1>), grid, block, 0, s, p);
-  }
+  (void)nct;
+  if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -222,6 +222,8 @@ def test_splitk_combine_standalone():
 
 @pytest.mark.parametrize("G", [1, 2, 4, 16])
 def test_prefill_group_sizes(G):
+    # tiles of 32 tokens up to G = 8, of 16 at G = 16 (one 16-column MFMA
+    # tile per wave)
     run_and_check(wl_custom(f"prefill_g{G}", [40, 100, 9], [0, 3000, 700], G=G, top_k=6),
                   per_seq=30)
 
