@@ -341,13 +341,20 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   // Keys of slots past the candidates are 0, below every candidate key and
   // below every trial value, so the counts need no per-slot guard (a
   // branch-free compare / ballot / popcount stream per bit).
+  // Once exactly kfree keys are at or above the threshold, no lower bit can
+  // change which keys those are (equal keys at the boundary never give an
+  // exact count), so the search stops there: for distinct scores that is
+  // about half of the 32 steps.
   uint32_t thr = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int s = 0; s < KPL; ++s) cnt += __popcll(ballot(key[s] >= cand));
-    if (cnt >= kfree) thr = cand;
+    if (cnt >= kfree) {
+      thr = cand;
+      if (cnt == kfree) break;
+    }
   }
   int above = 0;
 #pragma unroll
