@@ -12,8 +12,8 @@
 // take the partition's tiles in turn (wave w: tiles w, w + 4, ...), each
 // streaming its own tiles through its own ring of LDS stages with
 // global->LDS DMA, a whole ring of tiles in flight (four BF16 tiles, eight
-// FP8 ones), so no wave waits for another
-// inside the loop.  A wave holds all of the group's query heads as MFMA
+// FP8 ones), so no wave waits for another inside the loop.  A wave holds
+// all of the group's query heads as MFMA
 // columns (up to four 16-column tiles): S^T = X . Q^T over a tile (X the
 // 32 latent rows), an online softmax over the rows, then O^T += X^T . P^T
 // with X^T read from the same LDS tile by transposing reads -- keys and

@@ -245,3 +245,31 @@ def test_host_copy_of_generated_inputs_is_consistent():
     pb, orig = L.problem_for_sequences(inp, [0, 2], rows)
     sub = L.latent_attention(pb, [int(np.nonzero(orig == r)[0][0]) for r in rows])
     np.testing.assert_allclose(sub, full[rows], rtol=0, atol=0)
+
+
+def test_fp8_leaves_equal_their_bf16_encoding():
+    """Every e4m3 value is exactly a BF16 value, so a problem whose leaves are
+    stored as FP8 codes (generated inputs, NaN-poisoned slots included) must
+    give bit for bit the output of the same problem with the leaves re-encoded
+    as BF16 -- pinning the FP8 leaf path (codes, dtype plumbing, page-subset
+    copies) to the BF16 one.  The codes are decoded here by torch's own cast,
+    not by the oracle's table."""
+    wl = LI.LatentWorkload("t8", new_lens=(2, 1, 3), swa_cache_lens=(260, 40, 1000),
+                           comp_lens=(500, 90, 0), num_heads=8, num_latent_heads=2, window=48,
+                           top_c=40, sink_mean=1.0, bad_frac=0.1, dup_frac=0.1, seed=8,
+                           swa_dtype="fp8_e4m3", comp_dtype="fp8_e4m3", sigma=2.0)
+    inp = LI.make_latent_inputs(wl, "cpu")
+    pb8 = L.problem_from_inputs(inp)
+    pb16 = L.LatentProblem(**{**pb8.__dict__})
+    for leaf in ("swa_pool", "comp_pool"):
+        codes = torch.from_numpy(getattr(pb8, leaf).copy()).view(torch.float8_e4m3fn)
+        setattr(pb16, leaf, codes.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    pb16.swa_dtype = pb16.comp_dtype = "bf16"
+    out8 = L.latent_attention(pb8)
+    assert np.isfinite(out8).all()
+    np.testing.assert_array_equal(out8, L.latent_attention(pb16))
+    # the page-subset copy agrees too
+    rows = [0, 3, 5]
+    pb, orig = L.problem_for_sequences(inp, [0, 2], rows)
+    sub = L.latent_attention(pb, [int(np.nonzero(orig == r)[0][0]) for r in rows])
+    np.testing.assert_array_equal(sub, out8[rows])
