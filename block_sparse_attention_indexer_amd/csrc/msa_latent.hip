@@ -205,7 +205,10 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
       const int i = tid + 64 * kLatWaves * k;
       if (i < ntile * kLatentTile) {
         const char* a = nullptr;
-        if (pg[k] >= 0)
+        // a page id outside the pool (bad table data) is skipped like an
+        // invalid entry, so no read leaves the pool
+        const int npages = s < n_swa ? p.swa.pool.num_pages : p.comp.pool.num_pages;
+        if ((unsigned)pg[k] < (unsigned)npages)
           a = s < n_swa ? swa_base + (size_t)pg[k] * p.swa.pool.page_stride * ESZ +
                               (size_t)(ent[k] & 127) * p.swa.pool.token_stride * ESZ
                         : comp_base + (size_t)pg[k] * p.comp.pool.page_stride * ESZ +

@@ -39,7 +39,9 @@
  *     validation error the call returns a negative MSA_ERR_* code and
  *     enqueues nothing.  Device-data errors (a page id >= num_pages, a
  *     cache length beyond the lookup table) are not detected: their result
- *     is undefined.
+ *     is undefined.  Every kernel skips a page id outside [0, num_pages)
+ *     (as if that block or entry were not selected), so such data never
+ *     makes a read leave its pool.
  *   - Calls are stateless and may be issued from several host threads.
  *
  * Data layout:

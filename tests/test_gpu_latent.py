@@ -182,3 +182,28 @@ def test_running_max_moves_between_tiles(dtype):
              window=128, top_c=1024, scale=6.0 / 128 ** 0.5, seed=27, swa_dtype=dtype,
              comp_dtype=dtype),
           num_partitions=1)
+
+
+def test_page_ids_outside_the_pool_are_skipped():
+    # table entries pointing past the pool (or negative) make the entries on
+    # those pages count as not attended: the same output as listing none of
+    # them, and no read outside the pool
+    w = wl("lat_badpage", [1, 2], [700, 300], [900, 500], H=32, window=64, top_c=150, seed=31)
+    inp = LI.make_latent_inputs(w, DEV)
+    P = inp.comp_pool.shape[0]
+    tab = inp.comp_lookup_table.clone()
+    lists = inp.comp_indices.clone()
+    bad = {0: 2, 1: 1}                      # sequence -> logical page made bad
+    inp.comp_lookup_table[0, bad[0]] = P + 1000
+    inp.comp_lookup_table[1, bad[1]] = -7
+    got = B.run_latent(inp, num_partitions=2).clone()
+    offs = inp.input_row_offsets.cpu().tolist()
+    for b, lp in bad.items():
+        rows = lists[offs[b]:offs[b + 1]]
+        rows[(rows >= 128 * lp) & (rows < 128 * (lp + 1))] = -1
+    inp.comp_lookup_table.copy_(tab)
+    inp.comp_indices.copy_(lists)
+    ref = B.run_latent(inp, num_partitions=2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got.float()).all()
+    assert torch.equal(got, ref)
