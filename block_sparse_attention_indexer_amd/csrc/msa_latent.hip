@@ -64,6 +64,11 @@ struct LatentLds {
 
 __device__ __forceinline__ int lat_swz(int pos) { return ((pos & 7) << 1) | ((pos >> 3) & 1); }
 
+// entries a lookup-table row of `stride` pages addresses
+__device__ __forceinline__ int tab_cap(int stride) {
+  return stride > (0x7FFFFFFF >> 7) ? 0x7FFFFFFF : stride << 7;
+}
+
 // o *= s in place in the accumulation registers.  The accumulators live in
 // AGPRs (they are MFMA results and operands); written as plain C++, the
 // multiply makes the compiler copy every accumulator to VGPRs at the top of
@@ -142,8 +147,11 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     sink_v[ct] = p.sink[hl * p.G + (col_ok[ct] ? cg * 64 + 16 * ct + l16 : 0)];
   }
   const int r0 = p.offs[b], r1 = p.offs[b + 1];
-  const int swa_len = p.window > 0 ? p.swa.clen[b] : 0;
-  const int comp_len = p.top_c > 0 ? p.comp.clen[b] : 0;
+  // lengths past what a sequence's lookup table addresses (bad device data)
+  // are clipped to it, so no table read leaves the table's row (the host
+  // checked that the window leaf's table covers max_seq new positions more)
+  const int swa_len = p.window > 0 ? min(p.swa.clen[b], tab_cap(p.swa.stride) - p.max_seq) : 0;
+  const int comp_len = p.top_c > 0 ? min(p.comp.clen[b], tab_cap(p.comp.stride)) : 0;
   if (t >= min(r1 - r0, p.max_seq)) return;
   const int r = r0 + t;
 
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
 
   // ---- this partition's entries ---------------------------------------------
   const int pos = swa_len + t;
-  const int n_swa = p.window > 0 ? min(p.window, pos + 1) : 0;
+  const int n_swa = p.window > 0 ? max(0, min(p.window, pos + 1)) : 0;
   const int lo = pos - n_swa + 1;
   const int nent = n_swa + p.top_c;
   const int ntiles_row = (nent + kLatentTile - 1) / kLatentTile;

@@ -207,3 +207,18 @@ def test_page_ids_outside_the_pool_are_skipped():
     torch.cuda.synchronize()
     assert torch.isfinite(got.float()).all()
     assert torch.equal(got, ref)
+
+
+def test_lengths_past_the_lookup_table_stay_inside_it():
+    # a sequence whose device lengths exceed what its lookup tables address
+    # (bad data: its own result is undefined) must not disturb any other
+    # sequence's rows, which stay bit-identical to a clean call
+    w = wl("lat_badlen", [1, 2, 1], [700, 300, 1200], [900, 500, 300], H=16, window=64, top_c=120,
+           seed=32)
+    inp = LI.make_latent_inputs(w, DEV)
+    clean = B.run_latent(inp, num_partitions=2).clone()
+    inp.swa_cache_lengths[0] = 10 ** 9
+    inp.comp_cache_lengths[0] = 10 ** 9
+    got = B.run_latent(inp, num_partitions=2)
+    torch.cuda.synchronize()
+    assert torch.equal(got[1:], clean[1:])
