@@ -39,9 +39,10 @@
  *     validation error the call returns a negative MSA_ERR_* code and
  *     enqueues nothing.  Device-data errors (a page id >= num_pages, a
  *     cache length beyond the lookup table) are not detected: their result
- *     is undefined.  Every kernel skips a page id outside [0, num_pages)
- *     (as if that block or entry were not selected), so such data never
- *     makes a read leave its pool.
+ *     is undefined for the rows involved.  Every kernel either skips a
+ *     page id outside [0, num_pages) or reads page 0 in its place, and
+ *     clips lengths to what the lookup table addresses, so such data never
+ *     makes a read leave its pool or table.
  *   - Calls are stateless and may be issued from several host threads.
  *
  * Data layout:

@@ -183,6 +183,29 @@ def test_page_permutation_gives_bitwise_identical_results():
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
 
 
+@pytest.mark.parametrize("route", ["decode", "prefill"])
+def test_bad_page_ids_stay_inside_their_sequence(route):
+    # page ids outside the pool in one sequence's lookup table (bad data: that
+    # sequence's result is undefined) must leave every other sequence's
+    # selection and output bit-identical to a clean call; every kernel reads
+    # page 0 or skips the block instead, so no read leaves the pools
+    new = [1, 1, 1] if route == "decode" else [40, 100, 9]
+    wl = wl_custom(f"badpage_{route}", new, [3000, 5000, 700], top_k=6)
+    inp = I.make_inputs(wl, DEV)
+    d0 = B.run_indexer(inp).clone()
+    o0 = B.run_attention(inp, d0).clone()
+    P = inp.k_cache.shape[0]
+    inp.kv_lookup_table[0, 3] = P + 50
+    inp.kv_lookup_table[0, 10] = -3
+    d1 = B.run_indexer(inp)
+    o1 = B.run_attention(inp, d1)
+    torch.cuda.synchronize()
+    r1 = int(inp.input_row_offsets[1])
+    assert torch.equal(d0[r1:], d1[r1:])
+    assert torch.equal(o0[r1:].view(torch.int16), o1[r1:].view(torch.int16))
+    assert torch.isfinite(o1.float()).all()
+
+
 def test_rows_fully_written_and_no_ids_gives_zero():
     wl = wl_custom("poison", [1, 4], [3000, 500], top_k=5)
     inp = I.make_inputs(wl, DEV)
