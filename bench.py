@@ -309,7 +309,7 @@ def write_traffic_record(args):
     hbm = scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"]
     cmd = ("rocprofv3 --pmc {c} --kernel-include-regex "
            f"'{kernel_of(args.workload)}|combine_kernel|copy|elementwise' "
-           "--output-format csv -d $R/gpurun_out/pmc_{w}_{l} -o run -- python3 $R/bench.py "
+           "--output-format csv -d $OUT/pmc_{w}_{l} -o run -- python3 $R/bench.py "
            "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration")
     rec = {
         "kernel": (f"msa::{kernel_of(args.workload)}" if not raw["FETCH_SIZE"][4] else
@@ -332,10 +332,10 @@ def write_traffic_record(args):
         "commands": [cmd.format(c="FETCH_SIZE", w=args.workload, l="fetch"),
                      cmd.format(c="WRITE_SIZE", w=args.workload, l="write"),
                      f"python3 $R/bench.py --workload {args.workload} --traffic-record "
-                     f"$R/gpurun_out/pmc_{args.workload}_fetch/run_counter_collection.csv "
-                     f"$R/gpurun_out/pmc_{args.workload}_write/run_counter_collection.csv"],
-        "note": ("counter runs on the GPU box from /tmp with TMPDIR=/tmp; $R is the repository "
-                 "root. HBM bytes beyond the algorithmic gathered-KV bytes are q, the block ids, "
+                     f"$OUT/pmc_{args.workload}_fetch/run_counter_collection.csv "
+                     f"$OUT/pmc_{args.workload}_write/run_counter_collection.csv"],
+        "note": ("counter runs on an MI355X from /tmp with TMPDIR=/tmp; $R is the repository "
+                 "root and $OUT the directory the counter files go to. HBM bytes beyond the algorithmic gathered-KV bytes are q, the block ids, "
                  "page-table entries, the output (and split-K partials when the row is split), "
                  "the unused rows of partly filled blocks and blocks that several token groups "
                  "of one sequence load separately."),
@@ -618,7 +618,7 @@ def latent_cpu_baseline(inp, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path; "
+        sys.stderr.write("bench.py measures one GPU only: there is no multi-GPU path; "
                          "run with --gpus 1\n")
         sys.exit(2)
     import torch

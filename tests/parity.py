@@ -8,7 +8,7 @@ within 1e-3 of the oracle's cut.
 
 Attention parity: BF16 outputs within atol + rtol * |ref| of the oracle
 (1e-2 / 1e-2 for BF16 KV, 3e-2 / 3e-2 for FP8 KV), run on the oracle's own
-block ids so that selection and attention are judged separately.
+block ids so that selection and attention are checked separately.
 """
 from __future__ import annotations
 
