@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
     ap.add_argument("--partitions", type=int, default=0, help="split-K partitions (0 = auto)")
+    ap.add_argument("--entry", choices=("auto", "paged"), default="auto",
+                    help="attention entry point of a reuse step: auto = msa_attention_paged_shared, "
+                         "paged = msa_attention_paged (for comparison)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a kernel of known "
                          "traffic, to scale FETCH_SIZE / WRITE_SIZE counters)")
@@ -224,15 +227,41 @@ def is_latent(workload):
     return workload.startswith("latent")
 
 
+def is_reuse(workload):
+    return workload.endswith("_reuse")
+
+
 def kernel_of(workload):
-    return "latent_attn_kernel" if is_latent(workload) else "attn_decode_kernel"
+    """The dominant kernel of one attention call.  A reuse step calls
+    msa_attention_paged_shared, whose speculative rows run the union-tile
+    kernel."""
+    if is_latent(workload):
+        return "latent_attn_kernel"
+    return "attn_prefill3_kernel" if is_reuse(workload) else "attn_decode_kernel"
+
+
+def call_extra_kernels(workload):
+    """The other kernels one attention call launches."""
+    return ("prefill_plan_kernel", "attn_schedule_kernel") if is_reuse(workload) else ("combine_kernel",)
+
+
+def reuse_sources(inp):
+    """Source row of every row of a reuse step: its sequence's first row."""
+    import torch
+    offs = inp.input_row_offsets.cpu().numpy()
+    src = np.concatenate([np.full(offs[b + 1] - offs[b], offs[b]) for b in range(len(offs) - 1)])
+    return torch.from_numpy(src.astype(np.int32)).to(inp.input_row_offsets.device)
 
 
 def kernel_source_hash(workload="decode_batch64"):
     h = hashlib.sha256()
-    files = (("msa_latent.hip", "msa_latent.h", "msa_lds.h", "msa_attention.hip", "msa_common.h",
-              "msa_kernels.h")
-             if is_latent(workload) else ("msa_attention.hip", "msa_common.h", "msa_kernels.h"))
+    if is_latent(workload):
+        files = ("msa_latent.hip", "msa_latent.h", "msa_lds.h", "msa_attention.hip", "msa_common.h",
+                 "msa_kernels.h")
+    elif is_reuse(workload):
+        files = ("msa_prefill.hip", "msa_lds.h", "msa_common.h", "msa_kernels.h")
+    else:
+        files = ("msa_attention.hip", "msa_common.h", "msa_kernels.h")
     for f in files:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
@@ -285,13 +314,17 @@ def write_traffic_record(args):
         per = _counter_per_dispatch(path, counter)
         copy = max(v for name, vals in per.items() if "copy" in name.lower() for v in vals)
         attn = [v for name, vals in per.items() if kernel_of(args.workload) in name for v in vals]
-        comb = [v for name, vals in per.items() if "combine_kernel" in name for v in vals]
         if not attn:
             raise SystemExit(f"no {kernel_of(args.workload)} dispatch in {path}")
+        # the call's other kernels (the combine when split; the plan and
+        # schedule kernels of the union-tile route)
+        extra = 0.0
+        for k in call_extra_kernels(args.workload):
+            vals = [v for name, vs in per.items() if k in name for v in vs]
+            extra += float(np.mean(vals)) if vals else 0.0
         scale = COPY_BYTES / (copy * 1024.0)
-        # one attention call: the attention kernel, plus the combine when split
-        per_call = float(np.mean(attn)) + (float(np.mean(comb)) if comb else 0.0)
-        raw[counter] = (per_call, copy, scale, len(attn), float(np.mean(comb)) if comb else 0.0)
+        per_call = float(np.mean(attn)) + extra
+        raw[counter] = (per_call, copy, scale, len(attn), extra)
         scaled[counter] = per_call * 1024.0 * scale
 
     if is_latent(args.workload):
@@ -300,24 +333,27 @@ def write_traffic_record(args):
         algo = latent_work(LI.make_latent_inputs(lw, "cpu"))["latent_bytes"]
         wl_name = lw.name
     else:
-        wl = I.WORKLOADS[args.workload]()
+        wl = I.WORKLOADS[args.workload[:-len("_reuse")] if is_reuse(args.workload) else args.workload]()
         inp = I.make_inputs(wl, "cuda")
         d = B.run_indexer(inp)
+        if is_reuse(args.workload):
+            d = d[reuse_sources(inp).long()]
         torch.cuda.synchronize()
         algo = algorithmic_work(wl, d.cpu().numpy())["kv_bytes"]
         wl_name = wl.name
     hbm = scaled["FETCH_SIZE"] + scaled["WRITE_SIZE"]
     cmd = ("rocprofv3 --pmc {c} --kernel-include-regex "
-           f"'{kernel_of(args.workload)}|combine_kernel|copy|elementwise' "
+           f"'{'|'.join((kernel_of(args.workload),) + call_extra_kernels(args.workload))}|copy|elementwise' "
            "--output-format csv -d $OUT/pmc_{w}_{l} -o run -- python3 $R/bench.py "
            "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration")
     rec = {
         "kernel": (f"msa::{kernel_of(args.workload)}" if not raw["FETCH_SIZE"][4] else
-                   f"one attention call: msa::{kernel_of(args.workload)} + msa::combine_kernel"),
+                   "one attention call: " + " + ".join(
+                       f"msa::{k}" for k in (kernel_of(args.workload),) + call_extra_kernels(args.workload))),
         "workload": f"{args.workload} ({wl_name})",
         "fetch_size_kib_per_launch": raw["FETCH_SIZE"][0],
         "write_size_kib_per_launch": raw["WRITE_SIZE"][0],
-        "combine_fetch_write_kib_per_launch": [raw["FETCH_SIZE"][4], raw["WRITE_SIZE"][4]],
+        "other_kernels_fetch_write_kib_per_launch": [raw["FETCH_SIZE"][4], raw["WRITE_SIZE"][4]],
         "dispatches_averaged": raw["FETCH_SIZE"][3],
         "calibration": {
             "fetch_scale": raw["FETCH_SIZE"][2], "write_scale": raw["WRITE_SIZE"][2],
@@ -356,8 +392,11 @@ def run(workload, args):
     # "<workload>_reuse": a draft step that reuses an earlier step's block
     # selection (each row takes its sequence's first row's ids) instead of
     # running the indexer
-    reuse = workload.endswith("_reuse")
+    reuse = is_reuse(workload)
     wl = I.WORKLOADS[workload[:-len("_reuse")] if reuse else workload]()
+    # the reuse step's rows of a sequence share one selection: the shared entry
+    # point reads each sequence's blocks once for all of its tokens
+    shared = reuse and args.entry != "paged"
     prefill = wl.max_seq_length > 8
     inp = I.make_inputs(wl, "cuda")
     rg = B.ragged_of_inputs(inp)
@@ -379,16 +418,16 @@ def run(workload, args):
     if reuse:
         indexer()
         d_prev = d.clone()
-        offs = inp.input_row_offsets.cpu().numpy()
-        src = torch.from_numpy(np.concatenate(
-            [np.full(offs[b + 1] - offs[b], offs[b]) for b in range(wl.batch)]).astype(np.int32)).cuda()
+        src = reuse_sources(inp)
 
         def indexer():      # noqa: F811 - the draft step's selection
             B.msa_indexer_reuse(d, d_prev, src, stream)
 
+    attention_entry = B.msa_attention_paged_shared if shared else B.msa_attention_paged
+
     def attention():
-        B.msa_attention_paged(out, inp.q, d, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
-                              wl.num_kv_heads, wl.top_k, wl.softmax_scale, np_, ws_a, stream)
+        attention_entry(out, inp.q, d, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
+                        wl.num_kv_heads, wl.top_k, wl.softmax_scale, np_, ws_a, stream)
 
     for _ in range(args.warmup):
         indexer()
@@ -429,7 +468,7 @@ def run(workload, args):
     # The attention call also enqueues the combine when np > 1: time a combine
     # of the same shape on its own and subtract it.
     comb_ms = 0.0
-    if np_ > 1:
+    if np_ > 1 and not shared:
         rcap = wl.batch * wl.max_seq_length
         po = torch.zeros((np_, rcap, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
         pl = torch.zeros((np_, rcap, wl.num_q_heads), dtype=torch.float32, device="cuda")
@@ -465,8 +504,11 @@ def run(workload, args):
         unit = "GB/s"
         achieved = work["kv_bytes"] / (att_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload),
-                "kernel": "attn_decode_kernel" if np_ == 1 else
+                "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": traffic_record(workload) if shared == reuse else None,
+                "kernel": ("attention call (msa_attention_paged_shared): prefill_plan_kernel + "
+                           "attn_schedule_kernel + attn_prefill3_kernel (4 waves)") if shared else
+                          "attn_decode_kernel" if np_ == 1 else
                           "attention call: attn_decode_kernel + combine_kernel (split-K)"}
     res = {
         "metric": "decode gathered-KV GB/s (% HBM peak) + query tok/s; prefill TFLOP/s (% MFMA)",
@@ -481,7 +523,8 @@ def run(workload, args):
                    "gqa": wl.group, "top_k": wl.top_k, "init_blocks": wl.init_blocks,
                    "local_blocks": wl.local_blocks, "kv_dtype": wl.kv_dtype,
                    "index_k_heads": wl.num_ik_heads, "index_k_dtype": wl.ik_dtype,
-                   "split_k_partitions": np_},
+                   "split_k_partitions": 1 if shared else np_,
+                   "attention_entry": attention_entry.__name__},
         "query_tok_s": tok_s,
         "hbm_frac_of_step": (work["kv_bytes"] + work["ik_bytes"]) / (wall / K) / 1e9 / HBM_PEAK_GBPS,
         "gpu_ms_per_step": gpu_step_ms,

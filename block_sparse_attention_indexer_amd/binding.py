@@ -97,6 +97,11 @@ _SIGNATURES = {
         ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p]),
+    "msa_attention_paged_shared": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(PagedCache),
+        ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p]),
     "msa_latent_partitions": (ctypes.c_int, [ctypes.c_int32] * 7),
     "msa_latent_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 7),
     "msa_latent_attention_paged": (ctypes.c_int, [
@@ -248,19 +253,35 @@ def msa_indexer_reuse(d_indices, prev_indices, src_row, stream=None):
     return d_indices
 
 
+def _attention(name, output, q, d_indices, k_cache, v_cache, rg, num_q_heads, num_kv_heads,
+               top_k, scale, num_partitions, workspace, stream):
+    kc, vc = paged_cache(k_cache), paged_cache(v_cache)
+    need = msa_attention_workspace_bytes(rg, num_q_heads, num_kv_heads, top_k, num_partitions)
+    ws = _workspace(need, q.device, workspace)
+    st = getattr(library(), name)(_ptr(output), _ptr(q), _ptr(d_indices), ctypes.byref(kc),
+                                  ctypes.byref(vc), ctypes.byref(rg), num_q_heads, num_kv_heads,
+                                  top_k, float(scale), num_partitions, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, name)
+    return output
+
+
 def msa_attention_paged(output, q, d_indices, k_cache, v_cache, rg: Ragged, num_q_heads: int,
                         num_kv_heads: int, top_k: int, scale: float, num_partitions: int = 0,
                         workspace=None, stream=None):
     """Fill output [rows, H_q, 128] (bf16) with attention over the selected blocks."""
-    kc, vc = paged_cache(k_cache), paged_cache(v_cache)
-    need = msa_attention_workspace_bytes(rg, num_q_heads, num_kv_heads, top_k, num_partitions)
-    ws = _workspace(need, q.device, workspace)
-    st = library().msa_attention_paged(_ptr(output), _ptr(q), _ptr(d_indices), ctypes.byref(kc),
-                                       ctypes.byref(vc), ctypes.byref(rg), num_q_heads,
-                                       num_kv_heads, top_k, float(scale), num_partitions, _ptr(ws),
-                                       ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "msa_attention_paged")
-    return output
+    return _attention("msa_attention_paged", output, q, d_indices, k_cache, v_cache, rg,
+                      num_q_heads, num_kv_heads, top_k, scale, num_partitions, workspace, stream)
+
+
+def msa_attention_paged_shared(output, q, d_indices, k_cache, v_cache, rg: Ragged,
+                               num_q_heads: int, num_kv_heads: int, top_k: int, scale: float,
+                               num_partitions: int = 0, workspace=None, stream=None):
+    """msa_attention_paged for speculative steps whose rows of a sequence share
+    one selection (e.g. from msa_indexer_reuse): same result, each sequence's
+    block union is read once for all its tokens."""
+    return _attention("msa_attention_paged_shared", output, q, d_indices, k_cache, v_cache, rg,
+                      num_q_heads, num_kv_heads, top_k, scale, num_partitions, workspace, stream)
 
 
 def msa_splitk_combine(output, partial_o, partial_lse, input_row_offsets, batch: int,
@@ -346,15 +367,16 @@ def run_indexer(inp, d_indices=None, workspace=None, stream=None):
 
 
 def run_attention(inp, d_indices, output=None, num_partitions: int = 0, workspace=None,
-                  stream=None):
+                  stream=None, shared: bool = False):
+    """Attention of a problem; shared=True calls msa_attention_paged_shared."""
     wl = inp.wl
     rg = ragged_of_inputs(inp)
     if output is None:
         output = torch.empty((wl.total_rows, wl.num_q_heads, HEAD_DIM), dtype=torch.bfloat16,
                              device=inp.device)
-    return msa_attention_paged(output, inp.q, d_indices, inp.k_cache, inp.v_cache, rg,
-                               wl.num_q_heads, wl.num_kv_heads, wl.top_k, wl.softmax_scale,
-                               num_partitions, workspace, stream)
+    fn = msa_attention_paged_shared if shared else msa_attention_paged
+    return fn(output, inp.q, d_indices, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
+              wl.num_kv_heads, wl.top_k, wl.softmax_scale, num_partitions, workspace, stream)
 
 
 def latent_leaves_of_inputs(inp):

@@ -183,28 +183,33 @@ AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int re
   return pl;
 }
 
-// Prefill tiles: tokens per tile for group size G and KV type (the kernels'
-// choice).  Workspace is sized for the smaller tile of the two types, since
-// the size query does not know the type.
-int prefill_tokens_per_tile(int G, bool fp8) {
-  int tq = 0, nct = 0;
-  prefill_tiling(G, fp8, &tq, &nct);
-  return tq;
-}
-
-size_t prefill_plan_slots(const msa_ragged& rg, int G, int H_kv) {
-  const int tq = std::min(prefill_tokens_per_tile(G, false), prefill_tokens_per_tile(G, true));
+// Union-tile plan slots for `waves` waves per workgroup: tokens per tile
+// for group size G and KV type (the kernels' choice).  Workspace is sized
+// for the smaller tile of the two types, since the size query does not know
+// the type.
+size_t prefill_plan_slots(const msa_ragged& rg, int G, int H_kv, int waves) {
+  int tq_b = 0, tq_f = 0, nct = 0;
+  prefill_tiling(G, false, waves, &tq_b, &nct);
+  prefill_tiling(G, true, waves, &tq_f, &nct);
+  const int tq = std::min(tq_b, tq_f);
   return (size_t)rg.batch * ((rg.max_seq_length + tq - 1) / tq) * H_kv;
 }
 
-size_t attention_ws(const msa_ragged& rg, int H_q, int H_kv, int np) {
+// Workspace of the union-tile route: plan counts, ids, pages, masks, the
+// work list and the scheduler state.
+size_t union_ws(const msa_ragged& rg, int H_q, int H_kv, int waves) {
+  const size_t slots = prefill_plan_slots(rg, H_q / H_kv, H_kv, waves);
+  const size_t nb = (size_t)max_blocks(rg);
+  return 2 * align_up(slots * sizeof(int32_t)) + align_up(2 * sizeof(int32_t)) +
+         3 * align_up(slots * nb * sizeof(int32_t));
+}
+
+// Workspace one call needs: the union-tile route (prefill, and speculative
+// rows under msa_attention_paged_shared) or split-K partials.
+size_t attention_ws(const msa_ragged& rg, int H_q, int H_kv, int np, bool shared) {
   if (empty_batch(rg)) return 0;
-  if (route_of(rg) == Route::Prefill) {
-    const size_t slots = prefill_plan_slots(rg, H_q / H_kv, H_kv);
-    const size_t nb = (size_t)max_blocks(rg);
-    return 2 * align_up(slots * sizeof(int32_t)) + align_up(2 * sizeof(int32_t)) +
-           3 * align_up(slots * nb * sizeof(int32_t));
-  }
+  if (route_of(rg) == Route::Prefill) return union_ws(rg, H_q, H_kv, kUnionWavesPrefill);
+  if (shared && route_of(rg) == Route::Spec) return union_ws(rg, H_q, H_kv, kUnionWavesShared);
   if (np <= 1) return 0;
   const size_t rows = (size_t)np * row_capacity(rg) * H_q;
   return align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
@@ -490,14 +495,21 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t top_k, int32_t num_partitions) {
   const int np = msa_attention_partitions(rg, num_q_heads, num_kv_heads, top_k, num_partitions);
   if (np < 1) return 0;
-  return attention_ws(*rg, num_q_heads, num_kv_heads, np);
+  // Enough for either entry point: split-K partials, or the union-tile plan
+  // that msa_attention_paged_shared builds for speculative rows.
+  return std::max(attention_ws(*rg, num_q_heads, num_kv_heads, np, false),
+                  attention_ws(*rg, num_q_heads, num_kv_heads, np, true));
 }
 
-int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
-                        const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
-                        const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
-                        int32_t top_k, float scale, int32_t num_partitions, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+namespace {
+
+// Both attention entry points.  `shared` sends speculative rows through the
+// union-tile kernel (four waves per workgroup) instead of split-K decode.
+int attention_paged(void* output, const void* q, const int32_t* d_indices,
+                    const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                    const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads, int32_t top_k,
+                    float scale, int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                    void* stream, bool shared) {
   int st = check_ragged(rg);
   if (st != MSA_OK) return st;
   if ((st = check_heads(num_q_heads, num_kv_heads)) != MSA_OK) return st;
@@ -517,8 +529,11 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   int cus = 0;
   if (num_partitions == 0 && (st = current_device(&cus)) != MSA_OK) return st;
   const int G = num_q_heads / num_kv_heads;
-  const AttnPlan pl = plan_attention(*rg, G, num_kv_heads, top_k, num_partitions, cus);
-  const size_t need = attention_ws(*rg, num_q_heads, num_kv_heads, pl.np);
+  const Route route = route_of(*rg);
+  const bool union_tiles = route == Route::Prefill || (shared && route == Route::Spec);
+  AttnPlan pl = plan_attention(*rg, G, num_kv_heads, top_k, num_partitions, cus);
+  if (union_tiles) pl.np = 1;
+  const size_t need = attention_ws(*rg, num_q_heads, num_kv_heads, pl.np, shared);
   if (need && !workspace) return MSA_ERR_NULL;
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
   if (num_partitions != 0 && (st = current_device(&cus)) != MSA_OK) return st;
@@ -542,11 +557,12 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
   p.out = static_cast<uint16_t*>(output);
   const bool fp8 = k_cache->dtype == MSA_DTYPE_FP8_E4M3;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (route_of(*rg) == Route::Prefill) {
+  if (union_tiles) {
+    const int waves = route == Route::Prefill ? kUnionWavesPrefill : kUnionWavesShared;
     int nct = 0;
-    prefill_tiling(G, fp8, &p.tq, &nct);
+    prefill_tiling(G, fp8, waves, &p.tq, &nct);
     p.ntiles = (rg->max_seq_length + p.tq - 1) / p.tq;
-    const size_t slots = prefill_plan_slots(*rg, G, num_kv_heads);
+    const size_t slots = prefill_plan_slots(*rg, G, num_kv_heads, waves);
     char* w = static_cast<char*>(workspace);
     p.plan_cnt = reinterpret_cast<int32_t*>(w);
     w += align_up(slots * sizeof(int32_t));
@@ -561,7 +577,7 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
     p.sched = reinterpret_cast<int32_t*>(w);
     p.nwg = cus;   // one 142 KiB workgroup per CU
     if ((size_t)(p.nbmax + 1) * sizeof(uint32_t) > kMaxLds) return MSA_ERR_SHAPE;
-    if (launch_attention_prefill(p, fp8, s) != hipSuccess) return MSA_ERR_LAUNCH;
+    if (launch_attention_prefill(p, fp8, waves, s) != hipSuccess) return MSA_ERR_LAUNCH;
     return MSA_OK;
   }
   if (pl.np > 1) {
@@ -578,6 +594,26 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
     if (launch_combine(c, s) != hipSuccess) return MSA_ERR_LAUNCH;
   }
   return MSA_OK;
+}
+
+}  // namespace
+
+int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
+                        const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                        const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t top_k, float scale, int32_t num_partitions, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return attention_paged(output, q, d_indices, k_cache, v_cache, rg, num_q_heads, num_kv_heads,
+                         top_k, scale, num_partitions, workspace, workspace_bytes, stream, false);
+}
+
+int msa_attention_paged_shared(void* output, const void* q, const int32_t* d_indices,
+                               const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                               const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t top_k, float scale, int32_t num_partitions, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return attention_paged(output, q, d_indices, k_cache, v_cache, rg, num_q_heads, num_kv_heads,
+                         top_k, scale, num_partitions, workspace, workspace_bytes, stream, true);
 }
 
 int msa_splitk_combine(void* output, const float* partial_o, const float* partial_lse,

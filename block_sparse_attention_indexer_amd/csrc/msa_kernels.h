@@ -89,11 +89,15 @@ int prefill_indexer_tile(int H_kv, int H_ik);
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s);
 hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
-hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s);
+// Waves of the union-tile attention kernel per workgroup: the prefill route,
+// and speculative rows whose sequences share one selection.
+constexpr int kUnionWavesPrefill = 16;
+constexpr int kUnionWavesShared = 4;
+hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hipStream_t s);
 
-// Tokens per tile (tq) and MFMA column tiles per wave of the prefill
-// attention for group size G and KV storage type.
-void prefill_tiling(int G, bool fp8, int* tq, int* nct);
+// Tokens per tile (tq) and MFMA column tiles per wave of the union-tile
+// attention for group size G, KV storage type and waves per workgroup.
+void prefill_tiling(int G, bool fp8, int waves, int* tq, int* nct);
 
 // Bytes of LDS the decode attention kernel needs per workgroup.
 size_t attention_decode_lds_bytes(const AttnParams& p);

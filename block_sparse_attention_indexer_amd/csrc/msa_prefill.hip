@@ -449,7 +449,6 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams
 // 2k and 2k + 1 read the row holding P^T position k at dims 16dt and
 // 16dt + 8, and lane (m, g) receives the 8 positions of dim 16dt + m.
 // ---------------------------------------------------------------------------
-constexpr int kP3Waves = 16;
 constexpr float kLazy = 8.f;   // log2 headroom before the running max moves
 
 // Tile ring: 64 KiB each for K and V, i.e. two BF16 stages or four FP8
@@ -463,8 +462,11 @@ struct PrefillLds3 {
 };
 
 
-template <bool FP8, int NCT>
+// W waves share each staged block: 16 on the prefill route, 4 for the
+// speculative rows of one sequence (see launch_attention_prefill).
+template <bool FP8, int NCT, int W>
 __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L) {
+  constexpr int kP3Waves = W;
   constexpr int RB = FP8 ? 128 : 256;       // bytes per LDS tile row
   constexpr int ESZ = FP8 ? 1 : 2;          // bytes per cache element
   constexpr int TILE = kBlock * RB;         // bytes of one K (or V) tile
@@ -809,27 +811,27 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   }
 }
 
-template <bool FP8, int NCT>
-__global__ __launch_bounds__(64 * kP3Waves) void attn_prefill3_kernel(AttnParams p) {
+template <bool FP8, int NCT, int W>
+__global__ __launch_bounds__(64 * W) void attn_prefill3_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) PrefillLds3 lds;
   __shared__ int item_s;
   for (;;) {
     const int k = take_item(p.sched, &item_s);
     if (k < 0) break;
-    attn_prefill3_tile<FP8, NCT>(p, p.worklist[k], lds);
+    attn_prefill3_tile<FP8, NCT, W>(p, p.worklist[k], lds);
   }
 }
 
-void prefill_tiling(int G, bool /*fp8*/, int* tq, int* nct) {
-  // kP3Waves waves of at most 16 columns (one MFMA column tile), both KV
+void prefill_tiling(int G, bool /*fp8*/, int waves, int* tq, int* nct) {
+  // `waves` waves of at most 16 columns (one MFMA column tile), both KV
   // types.  Two column tiles per wave do not fit the 128 VGPRs a wave of a
   // 16-wave workgroup has: they spill inside the block loop (measured at
   // group size 16: 32.6 ms against 11.3 ms with 16-token tiles).
-  *tq = std::min(32, kP3Waves * 16 / G);
+  *tq = std::min(32, waves * 16 / G);
   *nct = 1;
 }
 
-hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s) {
+hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hipStream_t s) {
   const size_t slots = (size_t)p.rg.batch * p.ntiles * p.H_kv;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3((unsigned)slots), dim3(64),
                      (size_t)p.nbmax * sizeof(uint32_t), s, p);
@@ -838,12 +840,14 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, hipStream_t s
   hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), (size_t)(p.nbmax + 1) * sizeof(int), s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int tq, nct;
-  prefill_tiling(p.G, fp8, &tq, &nct);
-  const dim3 grid((unsigned)p.nwg), block(64 * kP3Waves);
-  (void)nct;
-  if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1>), grid, block, 0, s, p);
+  const dim3 grid((unsigned)p.nwg), block(64 * waves);
+  if (waves == kUnionWavesShared) {
+    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1, kUnionWavesShared>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1, kUnionWavesShared>), grid, block, 0, s, p);
+  } else {
+    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1, kUnionWavesPrefill>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1, kUnionWavesPrefill>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -224,8 +224,9 @@ int msa_attention_partitions(const msa_ragged* rg, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t top_k,
                              int32_t num_partitions);
 
-/* Workspace bytes msa_attention_paged needs (partials for the split-K
- * combine, and the prefill plan).  Returns 0 on invalid arguments. */
+/* Workspace bytes msa_attention_paged and msa_attention_paged_shared need
+ * (partials for the split-K combine, and the union-tile plan of prefill and
+ * of shared speculative steps).  Returns 0 on invalid arguments. */
 size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t top_k,
                                      int32_t num_partitions);
@@ -262,6 +263,34 @@ int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
                         const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t top_k, float scale, int32_t num_partitions,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same operation as msa_attention_paged, with the same arguments and
+ * result, scheduled for speculative steps whose rows of one sequence share
+ * one selection: draft steps that reuse a selection through
+ * msa_indexer_reuse ("DeepSeekSparseAttentionConfig" page,
+ * index_share_for_mtp_iteration field), with the per-token causality of the
+ * "msa" page's speculative route.
+ *
+ * When 2 <= max_seq_length <= 8, each group of tokens of a sequence (all of
+ * them, or 4 at group size 16) reads the union of its rows' blocks once,
+ * and the tokens share each staged block; num_partitions is then ignored
+ * and no combine runs.  Other shapes take msa_attention_paged's routes.  The
+ * result is correct for any selection and equals msa_attention_paged's
+ * within rounding; when the rows of a sequence select different blocks the
+ * union grows and this entry point is slower, so it is a scheduling hint,
+ * not a different operation.
+ *
+ * workspace     device, >= msa_attention_workspace_bytes(...) bytes (that
+ *               size covers both entry points).
+ *
+ * Errors: as msa_attention_paged.
+ */
+int msa_attention_paged_shared(void* output, const void* q, const int32_t* d_indices,
+                               const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                               const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t top_k, float scale, int32_t num_partitions,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Split-K combine ("msa" page: partials keyed on the ragged global query

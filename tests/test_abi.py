@@ -46,10 +46,14 @@ def indexer(r, c, heads=8, top_k=16, init=1, local=2, ws=0, d=FAKE, q=FAKE):
                                          local, FAKE if ws else None, ws, None)
 
 
-def attention(r, k, v, hq=64, hkv=8, top_k=16, np_=0, ws=0, out=FAKE, scale=0.1):
-    return B.library().msa_attention_paged(out, FAKE, FAKE, ctypes.byref(k), ctypes.byref(v),
-                                           ctypes.byref(r), hq, hkv, top_k, scale, np_,
-                                           FAKE if ws else None, ws, None)
+ATTENTION_ENTRIES = ("msa_attention_paged", "msa_attention_paged_shared")
+
+
+def attention(r, k, v, hq=64, hkv=8, top_k=16, np_=0, ws=0, out=FAKE, scale=0.1,
+              entry="msa_attention_paged"):
+    return getattr(B.library(), entry)(out, FAKE, FAKE, ctypes.byref(k), ctypes.byref(v),
+                                       ctypes.byref(r), hq, hkv, top_k, scale, np_,
+                                       FAKE if ws else None, ws, None)
 
 
 def test_indexer_validation():
@@ -119,9 +123,14 @@ def test_reuse_validation():
     assert lib.msa_indexer_reuse(FAKE, FAKE, FAKE, 1 << 20, 2, 64, 512, None) == SHAPE
 
 
-def test_attention_validation():
+@pytest.mark.parametrize("entry", ATTENTION_ENTRIES)
+def test_attention_validation(entry):
     k = cache(heads=8)
     v = cache(heads=8)
+
+    def attention(*a, **kw):
+        return globals()["attention"](*a, entry=entry, **kw)
+
     assert attention(rg(), k, v, out=None) == NULL
     assert attention(rg(), k, v, hq=60) == SHAPE
     assert attention(rg(), k, v, hq=8 * 32) == SHAPE              # group 32 unsupported
@@ -138,6 +147,24 @@ def test_attention_validation():
     need = B.msa_attention_workspace_bytes(rg(), 64, 8, 16, 4)
     assert attention(rg(), k, v, np_=4, ws=need - 1) == WORKSPACE
     assert attention(rg(batch=0), k, v) == OK
+
+
+def test_shared_speculative_steps_need_the_union_plan():
+    # One partition needs no partials, but the shared entry point's union-tile
+    # plan for 2-8 token rows still needs workspace; the query covers both.
+    k, v = cache(heads=8), cache(heads=8)
+    spec = rg(max_seq=4)
+    need = B.msa_attention_workspace_bytes(spec, 64, 8, 16, 1)
+    assert need > 0
+    assert attention(spec, k, v, np_=1, entry="msa_attention_paged_shared") == NULL
+    assert attention(spec, k, v, np_=1, ws=need - 1, entry="msa_attention_paged_shared") == WORKSPACE
+    assert attention(spec, k, v, np_=64, ws=need - 1, entry="msa_attention_paged_shared") == WORKSPACE
+    # decode rows (one token) take the split-K route under either entry point
+    dec = rg(max_seq=1)
+    assert B.msa_attention_workspace_bytes(dec, 64, 8, 16, 1) == 0
+    # the union plan grows with the sequences' tokens per tile at group size 16
+    assert (B.msa_attention_workspace_bytes(rg(max_seq=8), 256, 16, 16, 1)
+            > B.msa_attention_workspace_bytes(rg(max_seq=4), 256, 16, 16, 1))
 
 
 def test_partition_planning_is_host_only():

@@ -24,17 +24,20 @@ def _wl(name, new, cached, H_kv=2, G=8, top_k=6, kv="bf16"):
                       kv_sigma=0.5 if kv != "bf16" else 1.0, seed=21)
 
 
+# (problem, requested partitions, attention entry point)
 CASES = {
-    "decode_split": (_wl("g_decode", [1, 1, 1, 1], [9000, 3000, 130, 20000]), 3),
-    "spec": (_wl("g_spec", [3, 8, 1, 5], [6000, 2500, 700, 4000], top_k=8), 0),
-    "prefill": (_wl("g_prefill", [200, 45, 300], [1000, 5000, 0], top_k=5), 0),
-    "prefill_fp8": (_wl("g_prefill8", [100, 70], [3000, 600], top_k=5, kv="fp8_e4m3"), 0),
+    "decode_split": (_wl("g_decode", [1, 1, 1, 1], [9000, 3000, 130, 20000]), 3, False),
+    "spec": (_wl("g_spec", [3, 8, 1, 5], [6000, 2500, 700, 4000], top_k=8), 0, False),
+    "spec_shared": (_wl("g_spec_shared", [3, 8, 1, 5], [6000, 2500, 700, 4000], top_k=8), 0, True),
+    "prefill": (_wl("g_prefill", [200, 45, 300], [1000, 5000, 0], top_k=5), 0, False),
+    "prefill_fp8": (_wl("g_prefill8", [100, 70], [3000, 600], top_k=5, kv="fp8_e4m3"), 0, False),
 }
 
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_graph_replay_matches_eager(case):
-    wl, np_req = CASES[case]
+    wl, np_req, shared = CASES[case]
+    attention = B.msa_attention_paged_shared if shared else B.msa_attention_paged
     print(f"[case] graph {case}", flush=True)
     inp = I.make_inputs(wl, DEV)
     rg = B.ragged_of_inputs(inp)
@@ -50,9 +53,8 @@ def test_graph_replay_matches_eager(case):
     def step(d_buf, out_buf):
         B.msa_indexer_paged(d_buf, inp.q_idx, inp.index_k, rg, wl.num_kv_heads, wl.top_k,
                             wl.init_blocks, wl.local_blocks, ws_i)
-        B.msa_attention_paged(out_buf, inp.q, d_buf, inp.k_cache, inp.v_cache, rg,
-                              wl.num_q_heads, wl.num_kv_heads, wl.top_k, wl.softmax_scale, np_,
-                              ws_a)
+        attention(out_buf, inp.q, d_buf, inp.k_cache, inp.v_cache, rg, wl.num_q_heads,
+                  wl.num_kv_heads, wl.top_k, wl.softmax_scale, np_, ws_a)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

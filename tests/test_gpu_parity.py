@@ -292,19 +292,37 @@ def test_fp8_index_k_long_context_full_sampled():
 
 # --- selection reuse across draft steps ---------------------------------------
 
+def first_row_sources(inp):
+    """Each row's source for a reuse step: its sequence's first row."""
+    offs = inp.input_row_offsets.cpu().numpy()
+    return np.concatenate([np.full(offs[b + 1] - offs[b], offs[b])
+                           for b in range(len(offs) - 1)]).astype(np.int32)
+
+
+def oracle_reused_ids(inp, wl):
+    """The oracle's selection of every row, then each row given its
+    sequence's first row's ids; with the problem and its global rows."""
+    pb, orig = O.problem_for_sequences(inp, list(range(wl.batch)))
+    rows = list(range(len(orig)))
+    d_ref, _ = O.indexer(pb, rows)
+    full = np.full((wl.total_rows, wl.num_kv_heads, wl.top_k), -1, dtype=np.int32)
+    full[orig] = d_ref
+    return pb, orig, rows, full, full[first_row_sources(inp)]
+
+
 def test_reuse_gathers_rows_and_feeds_attention():
     # every draft token reuses its sequence's first token's selection; two
     # extra rows name out-of-range sources and must come back empty
     wl = wl_custom("reuse", [3, 8, 1, 5], [6000, 2500, 700, 4000], top_k=8)
+    say(f"[case] {wl.name}")
     inp = I.make_inputs(wl, DEV)
-    d_prev = B.run_indexer(inp)
-    offs = inp.input_row_offsets.cpu().numpy()
-    src = np.concatenate([np.full(offs[b + 1] - offs[b], offs[b]) for b in range(wl.batch)])
-    src_t = torch.from_numpy(src.astype(np.int32)).to(DEV)
+    pb, orig, rows, prev, reused = oracle_reused_ids(inp, wl)
+    d_prev = torch.from_numpy(prev).to(DEV)
+    src_t = torch.from_numpy(first_row_sources(inp)).to(DEV)
     d = torch.empty_like(d_prev)
     B.msa_indexer_reuse(d, d_prev, src_t)
     torch.cuda.synchronize()
-    assert torch.equal(d, d_prev[src_t.long()])
+    assert np.array_equal(d.cpu().numpy(), reused)
     bad = torch.tensor([-1, d_prev.shape[0]], dtype=torch.int32, device=DEV)
     d_bad = torch.empty((2,) + tuple(d_prev.shape[1:]), dtype=torch.int32, device=DEV)
     B.msa_indexer_reuse(d_bad, d_prev, bad)
@@ -313,7 +331,68 @@ def test_reuse_gathers_rows_and_feeds_attention():
     # attention on the reused selections, each row with its own causal clip
     out = B.run_attention(inp, d)
     torch.cuda.synchronize()
-    pb, orig = O.problem_for_sequences(inp, list(range(wl.batch)))
-    rows = list(range(len(orig)))
-    ref = O.attention(pb, d.cpu().numpy()[orig], rows)
+    ref = O.attention(pb, reused[orig], rows)
     parity.check_attention(out[torch.as_tensor(orig, device=DEV)], ref, wl.kv_dtype, "reuse")
+
+
+# --- msa_attention_paged_shared: speculative rows sharing one selection -------
+
+@pytest.mark.parametrize("G,kv", [(8, "bf16"), (8, "fp8_e4m3"), (16, "bf16"), (16, "fp8_e4m3"),
+                                  (1, "bf16"), (4, "bf16")])
+def test_shared_entry_on_reused_selections(G, kv):
+    # draft tokens reuse their sequence's first token's blocks; at group size
+    # 16 a tile holds 4 tokens, so 5-8 token sequences span a full tile and a
+    # ragged one; a 1-token sequence and one inside its first block ride along
+    wl = wl_custom(f"shared_G{G}_{kv}", [3, 8, 1, 5, 2, 7], [6000, 2500, 700, 4000, 20, 12000],
+                   G=G, top_k=8, kv=kv)
+    say(f"[case] {wl.name}")
+    inp = I.make_inputs(wl, DEV)
+    pb, orig, rows, _, reused = oracle_reused_ids(inp, wl)
+    d = torch.from_numpy(reused).to(DEV)
+    out = B.run_attention(inp, d, shared=True)
+    out_p = B.run_attention(inp, d)
+    torch.cuda.synchronize()
+    ref = O.attention(pb, reused[orig], rows)
+    g = torch.as_tensor(orig, device=DEV)
+    err = parity.check_attention(out[g], ref, kv, wl.name)
+    err_p = parity.check_attention(out_p[g], ref, kv, wl.name + " msa_attention_paged")
+    say(f"  rows={len(rows)} max|err| shared={err:.3e} paged={err_p:.3e}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_shared_entry_on_fresh_selections(kv):
+    # rows of a sequence select different blocks: the union grows, the result
+    # is the same operation's
+    wl = wl_custom(f"shared_fresh_{kv}", [3, 8, 1, 5], [6000, 2500, 700, 4000], top_k=8, kv=kv,
+                   seed=11)
+    say(f"[case] {wl.name}")
+    inp = I.make_inputs(wl, DEV)
+    pb, orig, rows, fresh, _ = oracle_reused_ids(inp, wl)
+    out = B.run_attention(inp, torch.from_numpy(fresh).to(DEV), shared=True)
+    torch.cuda.synchronize()
+    ref = O.attention(pb, fresh[orig], rows)
+    err = parity.check_attention(out[torch.as_tensor(orig, device=DEV)], ref, kv, wl.name)
+    say(f"  rows={len(rows)} max|err|={err:.3e}")
+
+
+def test_shared_entry_at_full_spec_size_sampled():
+    # the speculative workload's shape (batch 32, 2-8 drafts, contexts 8k-64k,
+    # top-k 32) as the reuse bench step runs it, sampled sequences
+    wl = I.spec_decode()
+    say(f"[case] {wl.name} shared, reused")
+    inp = I.make_inputs(wl, DEV)
+    seqs = [0, 9, 31]
+    pb, orig = O.problem_for_sequences(inp, seqs)
+    rows = list(range(len(orig)))
+    d_ref, _ = O.indexer(pb, rows)
+    # first row of each sampled sequence feeds every row of that sequence
+    offs = pb.input_row_offsets
+    src = np.concatenate([np.full(offs[b + 1] - offs[b], offs[b]) for b in range(len(seqs))])
+    reused = d_ref[src]
+    d = torch.full((wl.total_rows, wl.num_kv_heads, wl.top_k), -1, dtype=torch.int32, device=DEV)
+    d[torch.as_tensor(orig, device=DEV)] = torch.from_numpy(reused).to(DEV)
+    out = B.run_attention(inp, d, shared=True)
+    torch.cuda.synchronize()
+    ref = O.attention(pb, reused, rows)
+    err = parity.check_attention(out[torch.as_tensor(orig, device=DEV)], ref, wl.kv_dtype, wl.name)
+    say(f"  rows={len(rows)} max|err|={err:.3e}")
