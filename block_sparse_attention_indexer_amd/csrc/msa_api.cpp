@@ -61,6 +61,14 @@ int64_t max_blocks(const msa_ragged& rg) {
   return ((int64_t)rg.max_cache_length + rg.max_seq_length + MSA_BLOCK_SIZE - 1) / MSA_BLOCK_SIZE;
 }
 
+// Blocks the kernels may address per sequence: the host bound, and never
+// past the sequence's row of the lookup table, so that lengths beyond the
+// table (bad device data) cannot move a table read into the next row or
+// past the table.
+int32_t block_bound(const msa_ragged& rg) {
+  return (int32_t)std::min<int64_t>(max_blocks(rg), rg.lookup_stride);
+}
+
 int64_t row_capacity(const msa_ragged& rg) { return (int64_t)rg.batch * rg.max_seq_length; }
 
 int check_ragged(const msa_ragged* rg) {
@@ -331,7 +339,7 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   p.rg = ragged_of(*rg);
   p.scores = static_cast<float*>(workspace);
   p.d_indices = d_indices;
-  p.nbmax = (int32_t)max_blocks(*rg);
+  p.nbmax = block_bound(*rg);
   p.score_stride = (p.nbmax + 15) / 16 * 16;
   p.H_kv = num_kv_heads;
   p.H_ik = index_k->num_heads;
@@ -552,7 +560,7 @@ int attention_paged(void* output, const void* q, const int32_t* d_indices,
   p.ntg = pl.ntg;
   p.np = pl.np;
   p.rcap = (int32_t)row_capacity(*rg);
-  p.nbmax = (int32_t)max_blocks(*rg);
+  p.nbmax = block_bound(*rg);
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.out = static_cast<uint16_t*>(output);
   const bool fp8 = k_cache->dtype == MSA_DTYPE_FP8_E4M3;

@@ -409,6 +409,17 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
     cnt += __popcll(bal);
   }
   if (lane == 0) p.plan_cnt[slot] = cnt;
+  if (cnt == 0) {
+    // No token of the tile has a visible block: the work list holds
+    // non-empty slots only, so the tile's rows of this head group get their
+    // result, 0, here.  256-byte rows, written as 16-byte pieces.
+    const int pieces = ntok * p.G * (kDim * 2 / 16);
+    for (int i = lane; i < pieces; i += 64) {
+      const int row = i / (p.G * 16), head = (i / 16) % p.G, col = i % 16;
+      uint16_t* op = p.out + ((size_t)(r0 + t0 + row) * p.H_q + h * p.G + head) * kDim + 8 * col;
+      *reinterpret_cast<u32x4*>(op) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 }
 
 constexpr int kRingHalf = 256;   // plan entries per half of the LDS ring

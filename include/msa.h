@@ -135,7 +135,8 @@ typedef struct msa_ragged {
                                       /* this step's new tokens                  */
     const int32_t* kv_lookup_table;   /* device [batch][lookup_stride]: page id  */
                                       /* of each logical block                   */
-    int32_t lookup_stride;            /* entries per sequence in the table       */
+    int32_t lookup_stride;            /* entries per sequence in the table;      */
+                                      /* blocks at or past it are never read     */
     int32_t batch;                    /* sequences                               */
     int32_t max_seq_length;           /* host bound on new tokens per sequence;  */
                                       /* picks the route: 1 decode, 2..8         */

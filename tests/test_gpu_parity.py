@@ -24,11 +24,12 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_and_check(wl, seqs=None, per_seq=None, num_partitions=0):
-    say(f"[case] {wl.name} B={wl.batch} seqs={seqs} per_seq={per_seq} np={num_partitions}")
+def run_and_check(wl, seqs=None, per_seq=None, num_partitions=0, shared=False):
+    say(f"[case] {wl.name} B={wl.batch} seqs={seqs} per_seq={per_seq} np={num_partitions} "
+        f"shared={shared}")
     inp = I.make_inputs(wl, DEV)
     d_gpu = B.run_indexer(inp)
-    out_gpu = B.run_attention(inp, d_gpu, num_partitions=num_partitions)
+    out_gpu = B.run_attention(inp, d_gpu, num_partitions=num_partitions, shared=shared)
     torch.cuda.synchronize()
     seqs = list(range(wl.batch)) if seqs is None else list(seqs)
     pb, orig_rows = O.problem_for_sequences(inp, seqs)
@@ -38,7 +39,7 @@ def run_and_check(wl, seqs=None, per_seq=None, num_partitions=0):
     nd, nr = parity.check_selection(pb, sub, d_gpu[grows].cpu().numpy(), sels)
     d_mix = d_gpu.clone()
     d_mix[grows] = torch.from_numpy(d_ref).to(DEV)
-    out_mix = B.run_attention(inp, d_mix, num_partitions=num_partitions)
+    out_mix = B.run_attention(inp, d_mix, num_partitions=num_partitions, shared=shared)
     torch.cuda.synchronize()
     ref = O.attention(pb, d_ref, sub)
     err = parity.check_attention(out_mix[grows], ref, wl.kv_dtype, wl.name)
@@ -106,6 +107,7 @@ def test_fp8_spec_and_boosted_rows():
 def test_empty_and_zero_length_sequences():
     wl = wl_custom("zero_len", [1, 0, 3, 0], [900, 700, 2000, 10], top_k=4)
     run_and_check(wl)
+    run_and_check(wl, shared=True)
     inp = I.make_inputs(wl, DEV)
     rg = B.ragged(inp.input_row_offsets[:1], inp.cache_lengths[:0], inp.kv_lookup_table[:0], 0, 0)
     d = torch.empty((0, 2, 4), dtype=torch.int32, device=DEV)
@@ -183,22 +185,24 @@ def test_page_permutation_gives_bitwise_identical_results():
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
 
 
-@pytest.mark.parametrize("route", ["decode", "prefill"])
+@pytest.mark.parametrize("route", ["decode", "prefill", "spec_shared"])
 def test_bad_page_ids_stay_inside_their_sequence(route):
     # page ids outside the pool in one sequence's lookup table (bad data: that
     # sequence's result is undefined) must leave every other sequence's
     # selection and output bit-identical to a clean call; every kernel reads
     # page 0 or skips the block instead, so no read leaves the pools
-    new = [1, 1, 1] if route == "decode" else [40, 100, 9]
+    new = {"decode": [1, 1, 1], "prefill": [40, 100, 9], "spec_shared": [3, 8, 2]}[route]
+    shared = route == "spec_shared"
     wl = wl_custom(f"badpage_{route}", new, [3000, 5000, 700], top_k=6)
+    say(f"[case] {wl.name}")
     inp = I.make_inputs(wl, DEV)
     d0 = B.run_indexer(inp).clone()
-    o0 = B.run_attention(inp, d0).clone()
+    o0 = B.run_attention(inp, d0, shared=shared).clone()
     P = inp.k_cache.shape[0]
     inp.kv_lookup_table[0, 3] = P + 50
     inp.kv_lookup_table[0, 10] = -3
     d1 = B.run_indexer(inp)
-    o1 = B.run_attention(inp, d1)
+    o1 = B.run_attention(inp, d1, shared=shared)
     torch.cuda.synchronize()
     r1 = int(inp.input_row_offsets[1])
     assert torch.equal(d0[r1:], d1[r1:])
@@ -206,20 +210,70 @@ def test_bad_page_ids_stay_inside_their_sequence(route):
     assert torch.isfinite(o1.float()).all()
 
 
-def test_rows_fully_written_and_no_ids_gives_zero():
-    wl = wl_custom("poison", [1, 4], [3000, 500], top_k=5)
+@pytest.mark.parametrize("route", ["decode", "spec_shared", "prefill"])
+def test_lengths_past_the_lookup_table_stay_inside_it(route):
+    # the last sequence's device length (10^6) runs far past its lookup-table
+    # row, under a host bound on cache lengths four times the real one (so
+    # the host bound alone would allow blocks past the table): every kernel
+    # clips block counts to the table's width, so no read leaves the table,
+    # and the other sequences' ids and outputs stay bit-identical
+    new = {"decode": [1, 1, 1], "spec_shared": [3, 8, 2], "prefill": [40, 100, 9]}[route]
+    wl = wl_custom(f"longlen_{route}", new, [3000, 5000, 700], top_k=6)
+    say(f"[case] {wl.name}")
+    inp = I.make_inputs(wl, DEV)
+    rg = B.ragged(inp.input_row_offsets, inp.cache_lengths, inp.kv_lookup_table,
+                  wl.max_seq_length, 4 * wl.max_cache_length)
+    attention = B.msa_attention_paged_shared if route == "spec_shared" else B.msa_attention_paged
+
+    def step():
+        d = torch.empty((wl.total_rows, wl.num_kv_heads, wl.top_k), dtype=torch.int32, device=DEV)
+        B.msa_indexer_paged(d, inp.q_idx, inp.index_k, rg, wl.num_kv_heads, wl.top_k,
+                            wl.init_blocks, wl.local_blocks, index_k_scale=inp.index_k_scale)
+        out = torch.empty((wl.total_rows, wl.num_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+        attention(out, inp.q, d, inp.k_cache, inp.v_cache, rg, wl.num_q_heads, wl.num_kv_heads,
+                  wl.top_k, wl.softmax_scale)
+        return d, out
+
+    d_tight = B.run_indexer(inp).clone()
+    d0, o0 = step()
+    inp.cache_lengths[-1] = 10 ** 6
+    d1, o1 = step()
+    torch.cuda.synchronize()
+    assert torch.equal(d0, d_tight)              # the loose host bound changes nothing
+    rl = int(inp.input_row_offsets[-2])
+    assert torch.equal(d0[:rl], d1[:rl])
+    assert torch.equal(o0[:rl].view(torch.int16), o1[:rl].view(torch.int16))
+    assert torch.isfinite(o0.float()).all()
+
+
+@pytest.mark.parametrize("mode", ["paged", "shared", "prefill"])
+def test_rows_fully_written_and_no_ids_gives_zero(mode):
+    # decode + speculative rows through either entry point, or a prefill batch
+    # (whose tiles with no visible block are not in the work list)
+    shared = mode == "shared"
+    new = [1, 40] if mode == "prefill" else [1, 4]
+    wl = wl_custom("poison", new, [3000, 500], top_k=5)
+    say(f"[case] {wl.name} {mode}")
     inp = I.make_inputs(wl, DEV)
     d = B.run_indexer(inp)
     out = torch.full((wl.total_rows + 3, wl.num_q_heads, 128), float("nan"), dtype=torch.bfloat16,
                      device=DEV)
-    B.run_attention(inp, d, output=out)
+    B.run_attention(inp, d, output=out, shared=shared)
     torch.cuda.synchronize()
     assert torch.isfinite(out[:wl.total_rows].float()).all()
     assert torch.isnan(out[wl.total_rows:].float()).all()
     none = torch.full_like(d, -1)
-    B.run_attention(inp, none, output=out)
+    B.run_attention(inp, none, output=out, shared=shared)
     torch.cuda.synchronize()
     assert (out[:wl.total_rows].float() == 0).all()
+    # only blocks past every row's position: no visible position either
+    future = torch.full_like(d, -1)
+    future[:, :, 0] = 1000
+    out.fill_(float("nan"))
+    B.run_attention(inp, future, output=out, shared=shared)
+    torch.cuda.synchronize()
+    assert (out[:wl.total_rows].float() == 0).all()
+    assert torch.isnan(out[wl.total_rows:].float()).all()
 
 
 def test_splitk_combine_standalone():
