@@ -510,6 +510,21 @@ def run(workload, args):
                            "attn_schedule_kernel + attn_prefill3_kernel (4 waves)") if shared else
                           "attn_decode_kernel" if np_ == 1 else
                           "attention call: attn_decode_kernel + combine_kernel (split-K)"}
+    # The indexer call (scorer + top-k) against its own roof: index-K bytes
+    # over HBM peak on the decode routes, scoring flops over BF16 MFMA peak
+    # on the prefill route.  A reuse step runs no indexer, and rows that see
+    # no more than top_k blocks score nothing.
+    if reuse or idx_ms <= 0 or (work["ik_bytes"] == 0 and work["idx_flops"] == 0):
+        idx_roof = None
+    elif prefill:
+        a_idx = work["idx_flops"] / (idx_ms * 1e-3) / 1e12
+        idx_roof = {"bound": "mfma", "achieved": a_idx, "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": a_idx / BF16_MFMA_PEAK_TFLOPS,
+                    "call": "indexer_schedule_kernel + indexer_score_prefill_kernel + topk_kernel"}
+    else:
+        a_idx = work["ik_bytes"] / (idx_ms * 1e-3) / 1e9
+        idx_roof = {"bound": "hbm", "achieved": a_idx, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": a_idx / HBM_PEAK_GBPS, "call": "indexer_score_kernel + topk_kernel"}
     res = {
         "metric": "decode gathered-KV GB/s (% HBM peak) + query tok/s; prefill TFLOP/s (% MFMA)",
         "value": metric_value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -532,6 +547,7 @@ def run(workload, args):
                        "attention_kernel": attn_kernel_ms},
         "algorithmic": work,
         "roofline": roof,
+        "indexer_roofline": idx_roof,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, wl, prefill, args.cpu_seconds)

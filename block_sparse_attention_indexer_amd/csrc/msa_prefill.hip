@@ -433,7 +433,9 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams
 // ---------------------------------------------------------------------------
 // Prefill attention with direct global->LDS tile loads, BF16 or FP8 KV.
 //
-// Workgroup = 16 waves (four per SIMD), persistent over the slot work list;
+// Workgroup = W waves (16 on the prefill route, four per SIMD; 4 for the
+// speculative rows of msa_attention_paged_shared), persistent over the slot
+// work list;
 // wave w owns columns [w cpw, (w + 1) cpw) of the tile's tq * G (token,
 // query head) columns, as 16 * NCT MFMA columns.  K and V tiles are DMA'd
 // straight into LDS, row-major (256-byte rows for BF16, 128-byte rows for

@@ -108,6 +108,9 @@ def test_empty_and_zero_length_sequences():
     wl = wl_custom("zero_len", [1, 0, 3, 0], [900, 700, 2000, 10], top_k=4)
     run_and_check(wl)
     run_and_check(wl, shared=True)
+    # prefill route: empty sequences between long and one-token ones (empty
+    # plan slots and index tiles, a sequence with no cache)
+    run_and_check(wl_custom("zero_len_prefill", [0, 40, 0, 1, 17], [500, 3000, 0, 128, 0], top_k=4))
     inp = I.make_inputs(wl, DEV)
     rg = B.ragged(inp.input_row_offsets[:1], inp.cache_lengths[:0], inp.kv_lookup_table[:0], 0, 0)
     d = torch.empty((0, 2, 4), dtype=torch.int32, device=DEV)
