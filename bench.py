@@ -22,8 +22,12 @@ over those K steps.
 Roofline: the dominant kernel is the sparse-attention kernel.  Its duration
 is one attention call as the library enqueues it (the kernel, plus the
 split-K combine when the row is split), measured live with HIP events on the
-launch stream over K back-to-back calls; achieved = algorithmic bytes (or
-flops) of one call / that duration.
+launch stream around each call of K more steps run after the timed region
+(so each call sees the caches as a step leaves them); achieved = algorithmic
+bytes (or flops) of one call / that duration.  The same steps time the
+indexer call against its own roof (indexer_roofline).  cold_cache_ms adds
+the median of single calls after a 512 MiB read sweep of L2 and the
+last-level cache.
 
 Latent workloads (--workload latent_decode, latent_decode_fp8): one step is
 one msa_latent_attention_paged call; the metric is the latent bytes it must
@@ -67,6 +71,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
     ap.add_argument("--partitions", type=int, default=0, help="split-K partitions (0 = auto)")
+    ap.add_argument("--cold-runs", type=int, default=30,
+                    help="runs of the cold-cache per-call timing (median reported)")
     ap.add_argument("--entry", choices=("auto", "paged"), default="auto",
                     help="attention entry point of a reuse step: auto = msa_attention_paged_shared, "
                          "paged = msa_attention_paged (for comparison)")
@@ -267,6 +273,37 @@ def kernel_source_hash(workload="decode_batch64"):
     return h.hexdigest()[:16]
 
 
+FLUSH_BYTES = 512 * 2**20   # more than L2 (8 x 4 MB) plus the 256 MB last-level cache
+
+
+def cold_call_ms(fn, stream, runs):
+    """Median time of one call of `fn` on `stream` (HIP events around it),
+    each run preceded, outside the events, by a read of a 512 MiB scratch
+    buffer that evicts L2 and the last-level cache.  The sweep reads rather
+    than writes: a written sweep leaves up to 256 MB of dirty lines whose
+    write-back then lands inside the timed call.  None when runs is 0
+    (profiled runs pass --cold-runs 0 so that the trace holds only calls made
+    within steps)."""
+    import torch
+    if runs <= 0:
+        return None
+    scratch = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    scratch.sum()                 # write-back of the zeroing happens here
+    torch.cuda.synchronize()
+    times = []
+    for i in range(runs):
+        scratch.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    return float(np.median(times))
+
+
 def traffic_record(workload):
     """HBM traffic per launch of the attention kernel from committed rocprofv3
     counter runs, if they were taken on the current kernel source."""
@@ -345,7 +382,7 @@ def write_traffic_record(args):
     cmd = ("rocprofv3 --pmc {c} --kernel-include-regex "
            f"'{'|'.join((kernel_of(args.workload),) + call_extra_kernels(args.workload))}|copy|elementwise' "
            "--output-format csv -d $OUT/pmc_{w}_{l} -o run -- python3 $R/bench.py "
-           "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration")
+           "--workload {w} --steps 2 --warmup 1 --no-cpu-baseline --cold-runs 0 --copy-calibration")
     rec = {
         "kernel": (f"msa::{kernel_of(args.workload)}" if not raw["FETCH_SIZE"][4] else
                    "one attention call: " + " + ".join(
@@ -449,9 +486,23 @@ def run(workload, args):
     wall = time.perf_counter() - t0
     gpu_step_ms = t_start.elapsed_time(t_end) / K
 
-    # Per-call averages on the launch stream: K back-to-back calls of one
-    # entry point between two HIP events (an event between the calls of a
-    # step would itself add a gap to the step).
+    # Per-call averages in the step's own context: K more steps after the
+    # timed region, with HIP events around each call on the launch stream
+    # (kept out of the timed region, where they would add gaps).  Repeating
+    # one call alone would let its data stay in the 256 MB last-level cache
+    # (the FP8 128k attention reads 268 MB), which never happens within a
+    # step, where the other call's reads evict it.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for e in ev:
+        e[0].record(stream)
+        indexer()
+        e[1].record(stream)
+        attention()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    att_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+
     def per_call_ms(fn):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -462,8 +513,9 @@ def run(workload, args):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / K
 
-    att_ms = per_call_ms(attention)
-    idx_ms = per_call_ms(indexer)
+    cold = {"indexer_call": cold_call_ms(indexer, stream, args.cold_runs),
+            "attention_call": cold_call_ms(attention, stream, args.cold_runs),
+            "runs": args.cold_runs, "flush": f"{FLUSH_BYTES >> 20} MiB read", "statistic": "median"}
 
     # The attention call also enqueues the combine when np > 1: time a combine
     # of the same shape on its own and subtract it.
@@ -548,6 +600,7 @@ def run(workload, args):
         "algorithmic": work,
         "roofline": roof,
         "indexer_roofline": idx_roof,
+        "cold_cache_ms": cold,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, wl, prefill, args.cpu_seconds)
@@ -607,6 +660,8 @@ def run_latent(workload, args):
     # the roofline's duration: one call as the library enqueues it (kernel +
     # split-K combine), from the events around the timed steps
     achieved = work["latent_bytes"] / (gpu_ms * 1e-3) / 1e9
+    cold = {"latent_call": cold_call_ms(lambda: step(0), stream, args.cold_runs),
+            "runs": args.cold_runs, "flush": f"{FLUSH_BYTES >> 20} MiB read", "statistic": "median"}
     res = {
         "metric": "decode gathered-KV GB/s (% HBM peak) + query tok/s; prefill TFLOP/s (% MFMA)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -628,6 +683,7 @@ def run_latent(workload, args):
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload),
                      "kernel": "latent call: latent_attn_kernel" +
                                (" + combine_kernel (split-K)" if np_ > 1 else "")},
+        "cold_cache_ms": cold,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = latent_cpu_baseline(first, args.cpu_seconds)
