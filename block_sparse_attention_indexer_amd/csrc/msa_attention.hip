@@ -165,22 +165,34 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     // Addresses = wave-uniform base (page, head, half block, row constant)
     // + a 32-bit per-lane offset, so the loads take the scalar-base form.
     auto page_of = [&](int u) { return max(__builtin_amdgcn_readlane(pg_lane, u >> 1), 0); };
+    // A load whose rows all lie past the wave's last visible position in
+    // the half is pointed at the half's first rows instead, which other
+    // loads of the half fetch anyway (an L2 hit): its values are masked (K)
+    // or zeroed (V) later, so it need not fetch anything new from HBM.  The
+    // choice is wave-uniform and made on the scalar base, so every load stays
+    // unconditional and keeps its one per-lane offset.
+    auto last_row = [&](int u) {
+      return p_max - (__builtin_amdgcn_readlane(blk_lane, u >> 1) * kBlock + 64 * (u & 1));
+    };
     auto issue_k = [&](int u) {
       const char* kb = kpool + (size_t)page_of(u) * kps + khead + (size_t)(64 * (u & 1)) * kts;
+      const int lr = last_row(u);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const char* rowb = kb + (size_t)(16 * pt) * kts;
+        const char* rowb = kb + (size_t)(16 * pt > lr ? 0 : 16 * pt) * kts;
 #pragma unroll
         for (int s = 0; s < KW; ++s) kraw[pt][s] = ld16(rowb + koff + (FP8 ? 16 * s : 64 * s));
       }
     };
     auto issue_v = [&](int u) {
       const char* vb = vpool + (size_t)page_of(u) * vps + vhead + (size_t)(64 * (u & 1)) * vts;
+      const int lr = last_row(u);
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const char* rowb = vb + (size_t)(32 * ch + 16 * (j >> 2) + (j & 3)) * vts;
+          const int r0 = 32 * ch + 16 * (j >> 2) + (j & 3);   // the load's rows: r0 + 4 g
+          const char* rowb = vb + (size_t)(r0 > lr ? (j & 3) : r0) * vts;
           if constexpr (FP8) vraw[ch][j] = ld8(rowb + voff);
           else vraw[ch][j] = ld16(rowb + voff);
         }
