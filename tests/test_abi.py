@@ -2,6 +2,7 @@
 host-side validation rejects bad arguments before touching any device.
 CPU only: none of these calls reaches a kernel launch or a device query."""
 import ctypes
+import functools
 import re
 
 import pytest
@@ -127,10 +128,7 @@ def test_reuse_validation():
 def test_attention_validation(entry):
     k = cache(heads=8)
     v = cache(heads=8)
-
-    def attention(*a, **kw):
-        return globals()["attention"](*a, entry=entry, **kw)
-
+    attention = functools.partial(globals()["attention"], entry=entry)
     assert attention(rg(), k, v, out=None) == NULL
     assert attention(rg(), k, v, hq=60) == SHAPE
     assert attention(rg(), k, v, hq=8 * 32) == SHAPE              # group 32 unsupported
