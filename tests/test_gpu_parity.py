@@ -146,6 +146,11 @@ def test_maximum_context_and_top_k():
                             top_k=B.MSA_MAX_TOPK, init=1, local=4))
     run_and_check(wl_custom("max_prefill", [16], [full - 16], H_kv=1, G=4,
                             top_k=B.MSA_MAX_TOPK, init=1, local=4), per_seq=6)
+    # speculative rows through msa_attention_paged_shared: 8 tokens' fresh
+    # top-512 selections give a union of thousands of blocks per tile, so the
+    # 4-wave kernel's LDS ring of plan entries refills many times
+    run_and_check(wl_custom("max_spec_shared", [8, 5], [full - 8, 3000 * 128 + 5], H_kv=1, G=4,
+                            top_k=B.MSA_MAX_TOPK, init=1, local=4), per_seq=4, shared=True)
 
 
 def test_top_k_over_a_few_thousand_candidates():
