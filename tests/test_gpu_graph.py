@@ -142,3 +142,69 @@ def test_latent_graph_replay_matches_eager(np_req):
         torch.cuda.synchronize()
         assert torch.isfinite(out_g.float()).all(), f"replay {rep}"
         assert torch.equal(out_g, out_e), f"replay {rep}: graph output differs from eager"
+
+
+def test_calls_on_concurrent_streams_match_sequential():
+    """Calls keep no state between them: a split-K decode step, a prefill step
+    (persistent work list) and a split latent call enqueued on three streams
+    at once give, bit for bit, what they give one after another."""
+    from block_sparse_attention_indexer_amd import latent_inputs as LI
+    print("[case] concurrent streams", flush=True)
+    w_dec = _wl("cs_decode", [1, 1, 1, 1], [9000, 3000, 130, 20000])
+    w_pre = _wl("cs_prefill", [200, 45, 300], [1000, 5000, 0], top_k=5)
+    w_lat = LI.LatentWorkload("cs_latent", new_lens=(1, 3, 2), swa_cache_lens=(900, 4000, 130),
+                              comp_lens=(600, 1500, 40), num_heads=64, window=96, top_c=200,
+                              sink_mean=1.0, bad_frac=0.05, seed=29)
+
+    def msa_buffers(wl, np_req):
+        inp = I.make_inputs(wl, DEV)
+        rg = B.ragged_of_inputs(inp)
+        np_ = B.msa_attention_partitions(rg, wl.num_q_heads, wl.num_kv_heads, wl.top_k, np_req)
+        wsi = torch.empty(max(1, B.msa_indexer_workspace_bytes(rg, wl.num_kv_heads, wl.top_k)),
+                          dtype=torch.uint8, device=DEV)
+        wsa = torch.empty(max(1, B.msa_attention_workspace_bytes(rg, wl.num_q_heads,
+                                                                 wl.num_kv_heads, wl.top_k, np_)),
+                          dtype=torch.uint8, device=DEV)
+        d = torch.empty((wl.total_rows, wl.num_kv_heads, wl.top_k), dtype=torch.int32, device=DEV)
+        out = torch.empty((wl.total_rows, wl.num_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+
+        def step(stream=None):
+            B.run_indexer(inp, d_indices=d, workspace=wsi, stream=stream)
+            B.run_attention(inp, d, output=out, num_partitions=np_, workspace=wsa, stream=stream)
+        return step, (d, out)
+
+    step_dec, res_dec = msa_buffers(w_dec, 3)
+    step_pre, res_pre = msa_buffers(w_pre, 0)
+    lat = LI.make_latent_inputs(w_lat, DEV)
+    np_l = B.msa_latent_partitions(w_lat.batch, w_lat.max_seq_length, w_lat.num_heads, 1,
+                                   w_lat.window, w_lat.top_c, 3)
+    ws_l = torch.empty(max(1, B.msa_latent_workspace_bytes(w_lat.batch, w_lat.max_seq_length,
+                                                           w_lat.num_heads, 1, w_lat.window,
+                                                           w_lat.top_c, np_l)),
+                       dtype=torch.uint8, device=DEV)
+    out_l = torch.empty((w_lat.total_rows, w_lat.num_heads, 128), dtype=torch.bfloat16, device=DEV)
+
+    def step_lat(stream=None):
+        B.run_latent(lat, output=out_l, num_partitions=np_l, workspace=ws_l, stream=stream)
+
+    steps = (step_dec, step_pre, step_lat)
+    results = (res_dec, res_pre, (out_l,))
+    for f in steps:
+        f()
+    torch.cuda.synchronize()
+    ref = [[t.clone() for t in r] for r in results]
+    streams = [torch.cuda.Stream() for _ in steps]
+    for rep in range(3):
+        for r in results:
+            for t in r:
+                t.fill_(-1 if t.dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        for f, s in zip(steps, streams):
+            f(s)
+        torch.cuda.synchronize()
+        for r, rr in zip(results, ref):
+            for t, tt in zip(r, rr):
+                a = t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+                b = tt.view(torch.int16) if tt.dtype == torch.bfloat16 else tt
+                assert torch.equal(a, b), f"rep {rep}: a concurrent call differs from its sequential run"
+    print("  3 rounds of concurrent calls identical to sequential ones", flush=True)
