@@ -247,3 +247,25 @@ def test_latent_partition_planning():
     assert B.library().msa_latent_partitions(64, 1, 64, 1, 128, 1921, 1) == PARAM
     with pytest.raises(B.MsaError):
         B.msa_latent_partitions(4, 1, 64, 3, 128, 16, 0)
+
+
+def test_host_calls_from_many_threads_agree():
+    # ctypes drops the GIL for the call, so these run concurrently in the
+    # library: sizing queries and argument checks keep no shared state
+    from concurrent.futures import ThreadPoolExecutor
+    shapes = [rg(batch=b, max_seq=s, max_cache=c, stride=(c + s + 127) // 128 + 1)
+              for b, s, c in ((2, 1, 4000), (64, 1, 32767), (4, 8, 9000), (3, 300, 5000))]
+    k, v = cache(heads=8), cache(heads=8)
+
+    def one(i):
+        r = shapes[i % len(shapes)]
+        return (B.msa_attention_workspace_bytes(r, 64, 8, 16, 3),
+                B.msa_indexer_workspace_bytes(r, 8, 16),
+                B.msa_attention_partitions(r, 64, 8, 16, 5),
+                attention(r, k, v, np_=4, ws=0),
+                attention(r, k, v, hq=60))
+
+    expect = [one(i) for i in range(len(shapes))]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        got = list(ex.map(one, range(4000)))
+    assert all(g == expect[i % len(shapes)] for i, g in enumerate(got))
