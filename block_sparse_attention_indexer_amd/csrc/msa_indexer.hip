@@ -288,7 +288,9 @@ hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_
 }
 
 // ---------------------------------------------------------------------------
-// Top-k selection, one wave per (row, KV head).
+// Top-k selection, one wave per (row, HPW KV heads): HPW = 1, or several
+// on the prefill route, where the many rows make the per-wave setup and the
+// score loads' latency worth sharing between heads.
 //
 // Candidates are the blocks [init, nb - local) (everything not forced).  The
 // (top_k - |forced|)-th largest score is found by building its
@@ -299,78 +301,96 @@ hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_
 // prefix counts, so no sort is needed: forced-first, chosen candidates,
 // forced-newest are already ascending ranges.
 // ---------------------------------------------------------------------------
-template <int KPL>
+template <int KPL, int HPW>
 __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform((int)(threadIdx.x >> 6));
   const int b = blockIdx.y;
+  const int hgroups = (p.H_kv + HPW - 1) / HPW;
   const int idx = blockIdx.x * 4 + wave;
-  const int t = idx / p.H_kv;
-  const int h = idx % p.H_kv;
+  const int t = idx / hgroups;
+  const int h0 = (idx % hgroups) * HPW;
   const int r0 = p.rg.offs[b];
   const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
   if (t >= n) return;
+  const int nh = min(HPW, p.H_kv - h0);
   const int pos = p.rg.clen[b] + t;
   const int nb = min(pos / kBlock + 1, p.nbmax);
   const int r = r0 + t;
-  int32_t* out = p.d_indices + ((size_t)r * p.H_kv + h) * p.top_k;
+  int32_t* out0 = p.d_indices + ((size_t)r * p.H_kv + h0) * p.top_k;
   if (nb <= p.top_k) {
-    for (int i = lane; i < p.top_k; i += 64) out[i] = i < nb ? i : -1;
+    for (int i = lane; i < nh * p.top_k; i += 64) {
+      const int k = i % p.top_k;
+      out0[i] = k < nb ? k : -1;
+    }
     return;
   }
   const int ncand = nb - p.init - p.local;
   const int kfree = p.top_k - p.init - p.local;
-  for (int i = lane; i < p.init; i += 64) out[i] = i;
-  for (int i = lane; i < p.local; i += 64) out[p.init + kfree + i] = nb - p.local + i;
+  for (int hh = 0; hh < nh; ++hh) {
+    int32_t* out = out0 + (size_t)hh * p.top_k;
+    for (int i = lane; i < p.init; i += 64) out[i] = i;
+    for (int i = lane; i < p.local; i += 64) out[p.init + kfree + i] = nb - p.local + i;
+  }
   if (kfree == 0) return;
 
-  const float* sc = p.scores + ((size_t)r * p.H_kv + h) * p.score_stride + p.init;
+  const float* sc0 = p.scores + ((size_t)r * p.H_kv + h0) * p.score_stride + p.init;
   const int nslot = (ncand + 63) / 64;
-  // Slots holding candidates load (lanes past the end read the last one) with
-  // no use between the loads, so that they are all in flight together; keys
-  // past the candidates are 0, below every real key.
-  float v[KPL];
+  // Every head's candidate slots are requested before any is used (lanes
+  // past the end read the last candidate), so one memory latency covers
+  // the wave's heads; keys past the candidates are 0, below every real key.
+  float v[HPW][KPL];
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) v[s] = 0.f;
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-  for (int s = 0; s < KPL; ++s)
-    if (s < nslot) v[s] = sc[min(s * 64 + lane, ncand - 1)];
-  uint32_t key[KPL];
+    for (int s = 0; s < KPL; ++s) v[hh][s] = 0.f;
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) key[s] = s * 64 + lane < ncand ? score_key(v[s]) : 0u;
-  // Keys of slots past the candidates are 0, below every candidate key and
-  // below every trial value, so the counts need no per-slot guard (a
-  // branch-free compare / ballot / popcount stream per bit).
-  // Once exactly kfree keys are at or above the threshold, no lower bit can
-  // change which keys those are (equal keys at the boundary never give an
-  // exact count), so the search stops there: for distinct scores that is
-  // about half of the 32 steps.
-  uint32_t thr = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int s = 0; s < KPL; ++s) cnt += __popcll(ballot(key[s] >= cand));
-    if (cnt >= kfree) {
-      thr = cand;
-      if (cnt == kfree) break;
+    for (int s = 0; s < KPL; ++s)
+      if (hh < nh && s < nslot) v[hh][s] = sc0[(size_t)hh * p.score_stride + min(s * 64 + lane, ncand - 1)];
+
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    if (hh >= nh) break;
+    int32_t* out = out0 + (size_t)hh * p.top_k;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) key[s] = s * 64 + lane < ncand ? score_key(v[hh][s]) : 0u;
+    // Keys of slots past the candidates are 0, below every candidate key
+    // and below every trial value, so the counts need no per-slot guard (a
+    // branch-free compare / ballot / popcount stream per bit).  Once
+    // exactly kfree keys are at or above the threshold, no lower bit can
+    // change which keys those are (equal keys at the boundary never give an
+    // exact count), so the search stops there: for distinct scores that is
+    // about half of the 32 steps.
+    uint32_t thr = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int s = 0; s < KPL; ++s) cnt += __popcll(ballot(key[s] >= cand));
+      if (cnt >= kfree) {
+        thr = cand;
+        if (cnt == kfree) break;
+      }
     }
-  }
-  int above = 0;
+    int above = 0;
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) above += __popcll(ballot(key[s] > thr));
-  const int need_eq = kfree - above;
-  int run = 0, run_eq = 0;
+    for (int s = 0; s < KPL; ++s) above += __popcll(ballot(key[s] > thr));
+    const int need_eq = kfree - above;
+    int run = 0, run_eq = 0;
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    if (s < nslot) {
-    const bool eq = key[s] == thr;
-    const uint64_t em = ballot(eq);
-    const bool sel = key[s] > thr || (eq && run_eq + mask_rank(em) < need_eq);
-    const uint64_t sm = ballot(sel);
-    if (sel) out[p.init + run + mask_rank(sm)] = p.init + s * 64 + lane;
-    run += __popcll(sm);
-    run_eq += __popcll(em);
+    for (int s = 0; s < KPL; ++s) {
+      if (s < nslot) {
+        const bool eq = key[s] == thr;
+        const uint64_t em = ballot(eq);
+        const bool sel = key[s] > thr || (eq && run_eq + mask_rank(em) < need_eq);
+        const uint64_t sm = ballot(sel);
+        if (sel) out[p.init + run + mask_rank(sm)] = p.init + s * 64 + lane;
+        run += __popcll(sm);
+        run_eq += __popcll(em);
+      }
     }
   }
 }
@@ -400,11 +420,24 @@ hipError_t launch_indexer_reuse(int32_t* out, const int32_t* prev, const int32_t
 
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s) {
   const int ncand_max = p.nbmax - p.init - p.local;
-  dim3 grid((p.rg.max_seq * p.H_kv + 3) / 4, p.rg.batch);
-  if (ncand_max <= 256) hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, s, p);
-  else if (ncand_max <= 1024) hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, p);
-  else if (ncand_max <= 4096) hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(topk_kernel<128>, grid, dim3(256), 0, s, p);
+  // With many rows (the prefill route) one wave takes several KV heads of a
+  // token, paying the per-wave setup and the score loads' latency once.
+  const bool many = p.rg.max_seq > 8;
+  const dim3 block(256);
+  auto grid = [&](int hpw) {
+    return dim3((unsigned)((p.rg.max_seq * ((p.H_kv + hpw - 1) / hpw) + 3) / 4), (unsigned)p.rg.batch);
+  };
+  if (ncand_max <= 256) {
+    if (many) hipLaunchKernelGGL((topk_kernel<4, 8>), grid(8), block, 0, s, p);
+    else hipLaunchKernelGGL((topk_kernel<4, 1>), grid(1), block, 0, s, p);
+  } else if (ncand_max <= 1024) {
+    if (many) hipLaunchKernelGGL((topk_kernel<16, 2>), grid(2), block, 0, s, p);
+    else hipLaunchKernelGGL((topk_kernel<16, 1>), grid(1), block, 0, s, p);
+  } else if (ncand_max <= 4096) {
+    hipLaunchKernelGGL((topk_kernel<64, 1>), grid(1), block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<128, 1>), grid(1), block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
