@@ -6,13 +6,17 @@ in HBM: msa_indexer_paged (block-max scoring + top-k) then
 msa_attention_paged (sparse attention, plus the split-K combine when the row
 is split).  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_batch64]
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: decode, batch 64, 8 KV heads x GQA 8, context lengths
-uniform in [4096, 32768], top-k 16 (init 1, local 2), BF16 KV.  Its metric is
-the gathered-KV bytes the step must move divided by the step time (GB/s),
-with query tokens per second beside it; the prefill workload reports
-attention TFLOP/s instead.
+Default: the top-level fields are decode, batch 64, 8 KV heads x GQA 8,
+context lengths uniform in [4096, 32768], top-k 16 (init 1, local 2), BF16
+KV.  Its metric is the gathered-KV bytes the step must move divided by the
+step time (GB/s), with query tokens per second beside it.  The same line's
+"workloads" object holds every other workload measured in the same process
+with the same step count (the small decode, speculative decode, the ragged
+prefill -- which reports attention TFLOP/s --, the FP8 128k decode, and the
+FP8 index-K, selection-reuse and latent variants), each with its own
+roofline objects and a shorter oracle baseline.
 
 Timing: W untimed warmup steps, then exactly K steps bracketed by a device
 synchronize and two HIP events on the launch stream, with nothing else
@@ -63,10 +67,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_batch64",
+    ap.add_argument("--workload", default=None,
                     help="decode_small | decode_batch64 | spec_decode | prefill_ragged | "
                          "decode_fp8_long | decode_fp8_long_fp8ik | spec_decode_reuse | "
-                         "latent_decode | latent_decode_fp8 | all")
+                         "latent_decode | latent_decode_fp8 | all (one line each).  Default: "
+                         "one line for decode_batch64 whose 'workloads' object holds every "
+                         "other workload, measured in the same process")
+    ap.add_argument("--other-cpu-seconds", type=float, default=2.0,
+                    help="oracle budget of each workload inside the default line's 'workloads'")
+    ap.add_argument("--other-cold-runs", type=int, default=5,
+                    help="cold-cache runs of each workload inside the default line's 'workloads'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to sample for the CPU baseline")
@@ -743,14 +753,41 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     if args.traffic_record:
+        args.workload = args.workload or "decode_batch64"
         write_traffic_record(args)
         return
-    names = (["decode_small", "decode_batch64", "spec_decode", "prefill_ragged", "decode_fp8_long",
-              "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode", "latent_decode_fp8"]
-             if args.workload == "all" else [args.workload])
-    for name in names:
-        res = run_latent(name, args) if is_latent(name) else run(name, args)
-        print(json.dumps(res), flush=True)
+    everything = ["decode_small", "decode_batch64", "spec_decode", "prefill_ragged",
+                  "decode_fp8_long", "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode",
+                  "latent_decode_fp8"]
+
+    def one(name, a):
+        res = run_latent(name, a) if is_latent(name) else run(name, a)
+        torch.cuda.empty_cache()
+        return res
+
+    if args.workload is None:
+        # the headline workload, then every other one in the same process
+        # (shorter oracle and cold-cache budgets), folded into one line
+        head = one("decode_batch64", args)
+        sub = argparse.Namespace(**{**vars(args), "cpu_seconds": args.other_cpu_seconds,
+                                    "cold_runs": args.other_cold_runs})
+        others = {}
+        for name in everything:
+            if name == "decode_batch64":
+                continue
+            r = one(name, sub)
+            others[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "query_tok_s",
+                                              "gpu_ms_per_step", "dtype", "config", "kernels_ms",
+                                              "roofline", "indexer_roofline", "algorithmic",
+                                              "cold_cache_ms", "cpu_baseline") if k in r}
+            sys.stderr.write(f"{name}: {r['value']:.1f} {r['unit']}, {r['ms_per_step']:.4f} ms/step, "
+                             f"roofline frac {r['roofline']['frac']:.3f}\n")
+        head["workloads"] = others
+        print(json.dumps(head), flush=True)
+    else:
+        names = everything if args.workload == "all" else [args.workload]
+        for name in names:
+            print(json.dumps(one(name, args)), flush=True)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
         dst = torch.empty_like(src)

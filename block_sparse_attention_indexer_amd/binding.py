@@ -25,6 +25,7 @@ HEAD_DIM = 128
 MSA_MAX_SPEC_DRAFT = 8    # largest new-token count routed as speculative decode
 MSA_MAX_BLOCKS = 8192     # most blocks one sequence may hold
 MSA_MAX_TOPK = 512        # largest top_k
+MSA_MAX_KV_HEADS = 256    # most KV heads of one call
 
 
 class MsaError(RuntimeError):

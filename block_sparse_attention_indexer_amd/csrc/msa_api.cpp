@@ -224,7 +224,9 @@ size_t attention_ws(const msa_ragged& rg, int H_q, int H_kv, int np, bool shared
 }
 
 int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
-  if (num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads) return MSA_ERR_SHAPE;
+  if (num_kv_heads < 1 || num_kv_heads > MSA_MAX_KV_HEADS || num_q_heads < num_kv_heads ||
+      num_q_heads % num_kv_heads)
+    return MSA_ERR_SHAPE;
   const int G = num_q_heads / num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return MSA_ERR_SHAPE;
   return MSA_OK;
@@ -310,7 +312,9 @@ const char* msa_status_string(int status) {
 }
 
 size_t msa_indexer_workspace_bytes(const msa_ragged* rg, int32_t num_kv_heads, int32_t top_k) {
-  if (check_ragged(rg) != MSA_OK || num_kv_heads < 1 || top_k < 1) return 0;
+  if (check_ragged(rg) != MSA_OK || num_kv_heads < 1 || num_kv_heads > MSA_MAX_KV_HEADS ||
+      top_k < 1)
+    return 0;
   return indexer_ws(*rg, num_kv_heads, top_k);
 }
 
@@ -321,7 +325,9 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   int st = check_ragged(rg);
   if (st != MSA_OK) return st;
   if ((st = check_selection(top_k, init_blocks, local_blocks)) != MSA_OK) return st;
-  if (num_kv_heads < 1) return MSA_ERR_SHAPE;
+  // the prefill scorer's tile holds 256 (token, KV head) columns of one
+  // index-K head, so at most 256 KV heads may share it
+  if (num_kv_heads < 1 || num_kv_heads > MSA_MAX_KV_HEADS) return MSA_ERR_SHAPE;
   if (empty_batch(*rg)) return MSA_OK;   // no rows: buffers may be empty (null)
   if ((st = check_cache(index_k, CacheRole::IndexK)) != MSA_OK) return st;
   if (index_k->num_heads != 1 && index_k->num_heads != num_kv_heads) return MSA_ERR_SHAPE;

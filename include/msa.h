@@ -99,7 +99,8 @@ enum {
     MSA_HEAD_DIM = 128,      /* head dim of q, k, v, q_idx, k_idx   */
     MSA_MAX_SPEC_DRAFT = 8,  /* max_seq_length 2..8 takes the speculative route */
     MSA_MAX_BLOCKS = 8192,   /* most blocks one sequence may hold (1 Mi tokens) */
-    MSA_MAX_TOPK = 512
+    MSA_MAX_TOPK = 512,
+    MSA_MAX_KV_HEADS = 256   /* most KV heads (and index heads) of one call     */
 };
 
 /* One paged cache (a page pool of one layer). */
@@ -173,6 +174,7 @@ size_t msa_indexer_workspace_bytes(const msa_ragged* rg, int32_t num_kv_heads,
  * d_indices     device int32 [batch*max_seq_length rows max][num_kv_heads][top_k];
  *               rows >= input_row_offsets[batch] are not written.
  * q_idx         device bf16 [rows][num_kv_heads][128].
+ * num_kv_heads  1 .. MSA_MAX_KV_HEADS.
  * index_k       BF16 cache, or FP8 e4m3 cache with per-token scales (scale
  *               non-NULL), with num_heads 1 (shared by all KV heads) or
  *               num_kv_heads.
@@ -250,6 +252,7 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
  * d_indices     device int32 [rows][num_kv_heads][top_k] (the indexer's output).
  * k_cache, v_cache  caches with num_heads == num_kv_heads and the same dtype
  *               (BF16 or FP8 e4m3, scale-free: scale must be NULL).
+ * num_kv_heads  1 .. MSA_MAX_KV_HEADS.
  * num_q_heads   a multiple of num_kv_heads with group size 1, 2, 4, 8 or 16.
  * scale         softmax scale applied to q.k (e.g. 1/sqrt(128)); positive
  *               and finite.

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_function():
 
 def test_binding_constants_match_header():
     text = open(B.HEADER).read()
-    for name in ("MSA_MAX_SPEC_DRAFT", "MSA_MAX_BLOCKS", "MSA_MAX_TOPK", "MSA_DTYPE_BF16",
+    for name in ("MSA_MAX_SPEC_DRAFT", "MSA_MAX_BLOCKS", "MSA_MAX_TOPK", "MSA_MAX_KV_HEADS",
+                 "MSA_DTYPE_BF16",
                  "MSA_DTYPE_FP8_E4M3", "MSA_LATENT_MAX_TOPC"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m, name
@@ -79,6 +80,23 @@ def test_indexer_validation():
     assert need >= 2 * 8 * 32 * 4
     assert indexer(rg(), cache(), ws=need - 1) == WORKSPACE
     assert B.msa_indexer_workspace_bytes(rg(max_cache=1000), 8, 16) == 0   # nb <= top_k
+
+
+def test_kv_head_count_is_bounded_on_every_route():
+    # more than 256 KV heads per index-K head do not fit the prefill scorer's
+    # tile: rejected by the size query and the entry points on every route,
+    # before any arithmetic on the count
+    for max_seq in (1, 4, 64):
+        r = rg(max_seq=max_seq)
+        assert B.msa_indexer_workspace_bytes(r, 256, 16) > 0
+        for heads in (257, 300, 1 << 20):
+            assert B.msa_indexer_workspace_bytes(r, heads, 16) == 0
+            assert indexer(r, cache(), heads=heads) == SHAPE
+            assert indexer(r, cache(heads=heads), heads=heads) == SHAPE
+            k, v = cache(heads=heads), cache(heads=heads)
+            for entry in ATTENTION_ENTRIES:
+                assert attention(r, k, v, hq=heads, hkv=heads, entry=entry) == SHAPE
+            assert B.msa_attention_workspace_bytes(r, heads, heads, 16, 0) == 0
 
 
 def test_index_k_scale_rules():
