@@ -26,6 +26,7 @@ MSA_MAX_SPEC_DRAFT = 8    # largest new-token count routed as speculative decode
 MSA_MAX_BLOCKS = 8192     # most blocks one sequence may hold
 MSA_MAX_TOPK = 512        # largest top_k
 MSA_MAX_KV_HEADS = 256    # most KV heads of one call
+MSA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # msa_attention_paged_noalloc's fixed workspace
 
 
 class MsaError(RuntimeError):
@@ -103,6 +104,10 @@ _SIGNATURES = {
         ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p]),
+    "msa_attention_paged_noalloc": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(PagedCache),
+        ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]),
     "msa_latent_partitions": (ctypes.c_int, [ctypes.c_int32] * 7),
     "msa_latent_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 7),
     "msa_latent_attention_paged": (ctypes.c_int, [
@@ -283,6 +288,20 @@ def msa_attention_paged_shared(output, q, d_indices, k_cache, v_cache, rg: Ragge
     block union is read once for all its tokens."""
     return _attention("msa_attention_paged_shared", output, q, d_indices, k_cache, v_cache, rg,
                       num_q_heads, num_kv_heads, top_k, scale, num_partitions, workspace, stream)
+
+
+def msa_attention_paged_noalloc(output, q, d_indices, k_cache, v_cache, rg: Ragged,
+                                num_q_heads: int, num_kv_heads: int, top_k: int, scale: float,
+                                num_partitions: int = 0, stream=None):
+    """msa_attention_paged with no workspace argument: the library's fixed
+    per-GPU scratch array serves as the workspace (nothing is allocated)."""
+    kc, vc = paged_cache(k_cache), paged_cache(v_cache)
+    st = library().msa_attention_paged_noalloc(_ptr(output), _ptr(q), _ptr(d_indices),
+                                               ctypes.byref(kc), ctypes.byref(vc),
+                                               ctypes.byref(rg), num_q_heads, num_kv_heads, top_k,
+                                               float(scale), num_partitions, _stream(stream))
+    _check(st, "msa_attention_paged_noalloc")
+    return output
 
 
 def msa_splitk_combine(output, partial_o, partial_lse, input_row_offsets, batch: int,

@@ -307,6 +307,7 @@ const char* msa_status_string(int status) {
     case MSA_ERR_WORKSPACE: return "workspace too small";
     case MSA_ERR_LAUNCH: return "kernel launch failed";
     case MSA_ERR_DEVICE: return "no gfx950 device";
+    case MSA_ERR_SCRATCH: return "shape needs more workspace than the fixed scratch array holds";
     default: return "unknown status";
   }
 }
@@ -515,11 +516,13 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
                   attention_ws(*rg, num_q_heads, num_kv_heads, np, true));
 }
 
-namespace {
+}  // extern "C"
 
-// Both attention entry points.  `shared` sends speculative rows through the
+namespace msa {
+
+// All attention entry points.  `shared` sends speculative rows through the
 // union-tile kernel (four waves per workgroup) instead of split-K decode.
-int attention_paged(void* output, const void* q, const int32_t* d_indices,
+int attention_paged_entry(void* output, const void* q, const int32_t* d_indices,
                     const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
                     const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads, int32_t top_k,
                     float scale, int32_t num_partitions, void* workspace, size_t workspace_bytes,
@@ -610,15 +613,18 @@ int attention_paged(void* output, const void* q, const int32_t* d_indices,
   return MSA_OK;
 }
 
-}  // namespace
+}  // namespace msa
+
+extern "C" {
 
 int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
                         const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
                         const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t top_k, float scale, int32_t num_partitions, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return attention_paged(output, q, d_indices, k_cache, v_cache, rg, num_q_heads, num_kv_heads,
-                         top_k, scale, num_partitions, workspace, workspace_bytes, stream, false);
+  return msa::attention_paged_entry(output, q, d_indices, k_cache, v_cache, rg, num_q_heads,
+                                    num_kv_heads, top_k, scale, num_partitions, workspace,
+                                    workspace_bytes, stream, false);
 }
 
 int msa_attention_paged_shared(void* output, const void* q, const int32_t* d_indices,
@@ -626,8 +632,9 @@ int msa_attention_paged_shared(void* output, const void* q, const int32_t* d_ind
                                const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t top_k, float scale, int32_t num_partitions, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return attention_paged(output, q, d_indices, k_cache, v_cache, rg, num_q_heads, num_kv_heads,
-                         top_k, scale, num_partitions, workspace, workspace_bytes, stream, true);
+  return msa::attention_paged_entry(output, q, d_indices, k_cache, v_cache, rg, num_q_heads,
+                                    num_kv_heads, top_k, scale, num_partitions, workspace,
+                                    workspace_bytes, stream, true);
 }
 
 int msa_splitk_combine(void* output, const float* partial_o, const float* partial_lse,

@@ -3,7 +3,11 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+struct msa_paged_cache;
+struct msa_ragged;
 
 namespace msa {
 
@@ -101,5 +105,14 @@ void prefill_tiling(int G, bool fp8, int waves, int* tq, int* nct);
 
 // Bytes of LDS the decode attention kernel needs per workgroup.
 size_t attention_decode_lds_bytes(const AttnParams& p);
+
+// The body of the attention entry points (validation, plan, launches) with
+// the workspace given; `shared` picks the union-tile kernel for speculative
+// rows (msa_attention_paged_shared).
+int attention_paged_entry(void* output, const void* q, const int32_t* d_indices,
+                          const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                          const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t top_k, float scale, int32_t num_partitions, void* workspace,
+                          size_t workspace_bytes, void* stream, bool shared);
 
 }  // namespace msa

@@ -81,7 +81,9 @@ enum msa_status {
     MSA_ERR_DTYPE = -4,      /* unsupported storage type, or K and V types differ    */
     MSA_ERR_WORKSPACE = -5,  /* workspace smaller than the *_workspace_bytes query    */
     MSA_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch                    */
-    MSA_ERR_DEVICE = -7      /* no current HIP device, or it is not gfx950           */
+    MSA_ERR_DEVICE = -7,     /* no current HIP device, or it is not gfx950           */
+    MSA_ERR_SCRATCH = -8     /* msa_attention_paged_noalloc: the shape needs more    */
+                             /* workspace than its fixed device array holds         */
 };
 
 /* Storage types of the paged caches.  K/V ("msa" page): BF16 or native FP8
@@ -295,6 +297,34 @@ int msa_attention_paged_shared(void* output, const void* q, const int32_t* d_ind
                                const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t top_k, float scale, int32_t num_partitions,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * msa_attention_paged for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics, kernels and results as
+ * msa_attention_paged, without the workspace arguments: the workspace comes
+ * from one fixed device array of MSA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *
+ * Limit: a shape whose msa_attention_workspace_bytes(...) exceeds
+ * MSA_NOALLOC_SCRATCH_BYTES is rejected with MSA_ERR_SCRATCH before any
+ * launch (64 MiB hold, e.g., a 29,696-token prefill over 8 KV heads, or
+ * split-K decode partials of up to 8 partitions x 2048 rows x 64 heads).
+ *
+ * Sharing: every call on one GPU uses that GPU's one array, so calls that
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller; calls in order on one stream are safe.
+ *
+ * Errors: as msa_attention_paged, plus MSA_ERR_SCRATCH.
+ */
+enum { MSA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024 };
+
+int msa_attention_paged_noalloc(void* output, const void* q, const int32_t* d_indices,
+                                const msa_paged_cache* k_cache, const msa_paged_cache* v_cache,
+                                const msa_ragged* rg, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t top_k, float scale, int32_t num_partitions,
+                                void* stream);
 
 /*
  * Split-K combine ("msa" page: partials keyed on the ragged global query

@@ -32,6 +32,8 @@ def test_binding_constants_match_header():
         assert int(m.group(1)) == getattr(B, name), name
     m = re.search(r"\bMSA_LATENT_MAX_WINDOW\s*=\s*1\s*<<\s*(\d+)", text)
     assert m and 1 << int(m.group(1)) == B.MSA_LATENT_MAX_WINDOW
+    m = re.search(r"\bMSA_NOALLOC_SCRATCH_BYTES\s*=\s*(\d+)\s*\*\s*1024\s*\*\s*1024", text)
+    assert m and int(m.group(1)) << 20 == B.MSA_NOALLOC_SCRATCH_BYTES
 
 
 def rg(batch=2, max_seq=1, max_cache=4000, stride=40, null=False):
@@ -163,6 +165,31 @@ def test_attention_validation(entry):
     need = B.msa_attention_workspace_bytes(rg(), 64, 8, 16, 4)
     assert attention(rg(), k, v, np_=4, ws=need - 1) == WORKSPACE
     assert attention(rg(batch=0), k, v) == OK
+
+
+def noalloc(r, k, v, hq=64, hkv=8, top_k=16, np_=0, scale=0.1):
+    return B.library().msa_attention_paged_noalloc(FAKE, FAKE, FAKE, ctypes.byref(k), ctypes.byref(v),
+                                                   ctypes.byref(r), hq, hkv, top_k, scale, np_, None)
+
+
+def test_noalloc_entry_validation_and_scratch_limit():
+    SCRATCH = -8
+    k, v = cache(heads=8), cache(heads=8)
+    # argument errors are reported as by msa_attention_paged
+    assert noalloc(rg(), k, v, top_k=0) == PARAM
+    assert noalloc(rg(), k, v, hq=60) == SHAPE
+    assert noalloc(rg(), k, v, scale=0.0) == PARAM
+    assert noalloc(rg(batch=0), k, v) == OK
+    # a shape whose workspace exceeds the fixed array is rejected before any
+    # launch or device query (explicit partition count: host-only sizing)
+    big = rg(batch=2048, max_seq=1)
+    need = B.msa_attention_workspace_bytes(big, 64, 8, 16, 8)
+    assert need > B.MSA_NOALLOC_SCRATCH_BYTES
+    assert noalloc(big, k, v, np_=8) == SCRATCH
+    assert B.status_string(SCRATCH) != "unknown status"
+    # the ragged prefill (29,696 tokens, 8 KV heads, top-k 64) fits
+    pre = B.Ragged(FAKE, FAKE, FAKE, 256, 4, 16384, 16384)
+    assert 0 < B.msa_attention_workspace_bytes(pre, 64, 8, 64, 1) <= B.MSA_NOALLOC_SCRATCH_BYTES
 
 
 def test_shared_speculative_steps_need_the_union_plan():
