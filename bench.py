@@ -14,8 +14,9 @@ KV.  Its metric is the gathered-KV bytes the step must move divided by the
 step time (GB/s), with query tokens per second beside it.  The same line's
 "workloads" object holds every other workload measured in the same process
 with the same step count (the small decode, speculative decode, the ragged
-prefill -- which reports attention TFLOP/s --, the FP8 128k decode, and the
-FP8 index-K, selection-reuse and latent variants), each with its own
+prefill -- which reports attention TFLOP/s -- and its dense-causal and
+sparse sequences on their own, the FP8 128k decode, and the FP8 index-K,
+selection-reuse and latent variants), each with its own
 roofline objects and a shorter oracle baseline.
 
 Timing: W untimed warmup steps, then exactly K steps bracketed by a device
@@ -257,8 +258,11 @@ def kernel_of(workload):
 
 
 def call_extra_kernels(workload):
-    """The other kernels one attention call launches."""
-    return ("prefill_plan_kernel", "attn_schedule_kernel") if is_reuse(workload) else ("combine_kernel",)
+    """The other kernels one attention call launches (the latent call's
+    split-K combine; the plan and schedule kernels of the union-tile route)."""
+    if is_reuse(workload):
+        return ("prefill_plan_kernel", "attn_schedule_kernel")
+    return ("combine_kernel",) if is_latent(workload) else ()
 
 
 def reuse_sources(inp):
@@ -527,21 +531,8 @@ def run(workload, args):
             "attention_call": cold_call_ms(attention, stream, args.cold_runs),
             "runs": args.cold_runs, "flush": f"{FLUSH_BYTES >> 20} MiB read", "statistic": "median"}
 
-    # The attention call also enqueues the combine when np > 1: time a combine
-    # of the same shape on its own and subtract it.
-    comb_ms = 0.0
-    if np_ > 1 and not shared:
-        rcap = wl.batch * wl.max_seq_length
-        po = torch.zeros((np_, rcap, wl.num_q_heads, 128), dtype=torch.float32, device="cuda")
-        pl = torch.zeros((np_, rcap, wl.num_q_heads), dtype=torch.float32, device="cuda")
-        torch.cuda.synchronize()
-        comb_ms = per_call_ms(lambda: B.msa_splitk_combine(out, po, pl, inp.input_row_offsets,
-                                                            wl.batch, wl.max_seq_length, np_,
-                                                            wl.num_q_heads, stream))
-        attention()                       # restore the real output
-        torch.cuda.synchronize()
-    attn_kernel_ms = max(att_ms - comb_ms, 1e-6)
-
+    # Split-K partials are merged inside the attention kernel (no combine
+    # launch), so the attention call is the attention kernel.
     work = algorithmic_work(wl, d.cpu().numpy())
     if reuse:
         # the reused selection reads no index-K and scores nothing
@@ -571,7 +562,7 @@ def run(workload, args):
                 "kernel": ("attention call (msa_attention_paged_shared): prefill_plan_kernel + "
                            "attn_schedule_kernel + attn_prefill3_kernel (4 waves)") if shared else
                           "attn_decode_kernel" if np_ == 1 else
-                          "attention call: attn_decode_kernel + combine_kernel (split-K)"}
+                          "attn_decode_kernel (split-K, partials merged in-kernel)"}
     # The indexer call (scorer + top-k) against its own roof: index-K bytes
     # over HBM peak on the decode routes, scoring flops over BF16 MFMA peak
     # on the prefill route.  A reuse step runs no indexer, and rows that see
@@ -605,8 +596,7 @@ def run(workload, args):
         "query_tok_s": tok_s,
         "hbm_frac_of_step": (work["kv_bytes"] + work["ik_bytes"]) / (wall / K) / 1e9 / HBM_PEAK_GBPS,
         "gpu_ms_per_step": gpu_step_ms,
-        "kernels_ms": {"indexer_call": idx_ms, "attention_call": att_ms, "combine": comb_ms,
-                       "attention_kernel": attn_kernel_ms},
+        "kernels_ms": {"indexer_call": idx_ms, "attention_call": att_ms},
         "algorithmic": work,
         "roofline": roof,
         "indexer_roofline": idx_roof,
@@ -757,7 +747,7 @@ def main():
         write_traffic_record(args)
         return
     everything = ["decode_small", "decode_batch64", "spec_decode", "prefill_ragged",
-                  "decode_fp8_long", "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode",
+                  "prefill_ragged_dense", "prefill_ragged_sparse", "decode_fp8_long", "decode_fp8_long_fp8ik", "spec_decode_reuse", "latent_decode",
                   "latent_decode_fp8"]
 
     def one(name, a):

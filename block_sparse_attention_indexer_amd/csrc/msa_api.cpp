@@ -158,13 +158,23 @@ struct AttnPlan {
   int tpw, ntg, np;
 };
 
+// Tokens per wave and waves (token groups) per workgroup of the decode
+// kernel, and the workgroups of token groups per (sequence, KV head).
+void decode_tiling(const msa_ragged& rg, int G, int* tpw, int* ntg, int* ntgb) {
+  const Route r = route_of(rg);
+  *tpw = r == Route::Decode ? 1 : std::min(16 / G, std::max(1, rg.max_seq_length));
+  if (r == Route::Prefill) *tpw = 16 / G;
+  const int ntok_groups = (rg.max_seq_length + *tpw - 1) / *tpw;
+  *ntg = std::min(4, ntok_groups);
+  *ntgb = (ntok_groups + *ntg - 1) / *ntg;
+}
+
 AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int req_np, int cus) {
   AttnPlan pl{};
   const Route r = route_of(rg);
-  pl.tpw = r == Route::Decode ? 1 : std::min(16 / G, std::max(1, rg.max_seq_length));
-  if (r == Route::Prefill) pl.tpw = 16 / G;
+  int ntgb = 0;
+  decode_tiling(rg, G, &pl.tpw, &pl.ntg, &ntgb);
   const int ntok_groups = (rg.max_seq_length + pl.tpw - 1) / pl.tpw;
-  pl.ntg = std::min(4, ntok_groups);
   if (r == Route::Prefill) {
     pl.np = 1;
     return pl;
@@ -208,8 +218,32 @@ size_t prefill_plan_slots(const msa_ragged& rg, int G, int H_kv, int waves) {
 size_t union_ws(const msa_ragged& rg, int H_q, int H_kv, int waves) {
   const size_t slots = prefill_plan_slots(rg, H_q / H_kv, H_kv, waves);
   const size_t nb = (size_t)max_blocks(rg);
-  return 2 * align_up(slots * sizeof(int32_t)) + align_up(2 * sizeof(int32_t)) +
+  return 2 * align_up(slots * sizeof(int32_t)) + align_up(kSchedInts * sizeof(int32_t)) +
          3 * align_up(slots * nb * sizeof(int32_t));
+}
+
+// Split-K workspace of the decode kernel: the ready flags (one per
+// partition of each workgroup of token groups of a (sequence, KV head)),
+// then the partial outputs and log-sum-exps of every partition.
+size_t splitk_counters(const msa_ragged& rg, int G, int H_kv) {
+  int tpw = 0, ntg = 0, ntgb = 0;
+  decode_tiling(rg, G, &tpw, &ntg, &ntgb);
+  return (size_t)rg.batch * H_kv * ntgb;
+}
+
+size_t splitk_ws(const msa_ragged& rg, int H_q, int H_kv, int np) {
+  const size_t rows = (size_t)np * row_capacity(rg) * H_q;
+  return align_up(splitk_counters(rg, H_q / H_kv, H_kv) * np * sizeof(uint64_t)) +
+         align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+// Epoch stamped into a call's split-K ready flags: never 0, new per call.
+std::atomic<uint64_t> g_epoch{0};
+uint64_t next_epoch() {
+  for (;;) {
+    const uint64_t e = g_epoch.fetch_add(1) + 1;
+    if (e) return e;
+  }
 }
 
 // Workspace one call needs: the union-tile route (prefill, and speculative
@@ -219,8 +253,7 @@ size_t attention_ws(const msa_ragged& rg, int H_q, int H_kv, int np, bool shared
   if (route_of(rg) == Route::Prefill) return union_ws(rg, H_q, H_kv, kUnionWavesPrefill);
   if (shared && route_of(rg) == Route::Spec) return union_ws(rg, H_q, H_kv, kUnionWavesShared);
   if (np <= 1) return 0;
-  const size_t rows = (size_t)np * row_capacity(rg) * H_q;
-  return align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
+  return splitk_ws(rg, H_q, H_kv, np);
 }
 
 int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
@@ -598,18 +631,19 @@ int attention_paged_entry(void* output, const void* q, const int32_t* d_indices,
     return MSA_OK;
   }
   if (pl.np > 1) {
+    // counters, partial outputs, partial log-sum-exps; the kernel's last
+    // partition of each group merges (no separate combine launch)
     const size_t rows = (size_t)pl.np * p.rcap * num_q_heads;
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align_up(rows * MSA_HEAD_DIM * sizeof(float)));
+    char* w = static_cast<char*>(workspace);
+    p.ready = reinterpret_cast<uint64_t*>(w);
+    w += align_up(splitk_counters(*rg, G, num_kv_heads) * pl.np * sizeof(uint64_t));
+    p.part_o = reinterpret_cast<float*>(w);
+    w += align_up(rows * MSA_HEAD_DIM * sizeof(float));
+    p.part_lse = reinterpret_cast<float*>(w);
+    p.epoch = next_epoch();
   }
   if (attention_decode_lds_bytes(p) > kMaxLds) return MSA_ERR_PARAM;
   if (launch_attention_decode(p, fp8, s) != hipSuccess) return MSA_ERR_LAUNCH;
-  if (pl.np > 1) {
-    CombineParams c{p.part_o, p.part_lse, rg->input_row_offsets, p.out, rg->batch,
-                    rg->max_seq_length, pl.np, num_q_heads, p.rcap};
-    if (launch_combine(c, s) != hipSuccess) return MSA_ERR_LAUNCH;
-  }
   return MSA_OK;
 }
 

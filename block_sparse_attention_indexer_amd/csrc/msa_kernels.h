@@ -63,14 +63,19 @@ struct AttnParams {
   uint16_t* out;          // bf16 [R][H_q][128]
   float* part_o;          // [np][rcap][H_q][128]
   float* part_lse;        // [np][rcap][H_q]
+  // split-K ready flags, [group of token groups of a (sequence, KV head)][np]:
+  // a partition stores the call's epoch when its partial is complete; the
+  // merging partition (np - 1) clears them
+  uint64_t* ready;
+  uint64_t epoch;         // per call, never 0
   // prefill route: tiles of tq tokens and the device-built plan
   int32_t tq, ntiles;     // tokens per tile, tiles per sequence
   int32_t* plan_cnt;      // [B][ntiles][H_kv] union size
   int32_t* plan_ids;      // [B][ntiles][H_kv][nbmax] ascending block ids
   int32_t* plan_pages;    // [B][ntiles][H_kv][nbmax] page id of each block
   uint32_t* plan_mask;    // [B][ntiles][H_kv][nbmax] token mask per block
-  int32_t* worklist;      // [B * ntiles * H_kv] non-empty plan slots, heaviest first
-  int32_t* sched;         // [0] slots in the list, [1] next slot to take
+  int32_t* worklist;      // [B * ntiles * H_kv] non-empty plan slots, one list per XCD
+  int32_t* sched;         // kSchedInts: per XCD list, its length, next entry and start
   int32_t nwg;            // persistent workgroups launched
 };
 
@@ -93,6 +98,8 @@ int prefill_indexer_tile(int H_kv, int H_ik);
 hipError_t launch_topk(const IndexerParams& p, hipStream_t s);
 hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+// Ints of the union-tile route's scheduler state (three per XCD list).
+constexpr int kSchedInts = 24;
 // Waves of the union-tile attention kernel per workgroup: the prefill route,
 // and speculative rows whose sequences share one selection.
 constexpr int kUnionWavesPrefill = 16;

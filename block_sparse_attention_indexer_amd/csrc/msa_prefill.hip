@@ -98,6 +98,141 @@ __device__ void schedule_by_cost(int nitems, int maxcost, Cost cost, int32_t* li
   }
 }
 
+// ---------------------------------------------------------------------------
+// XCD-clustered work lists.  The chip's 256 CUs sit in 8 XCDs, each with
+// its own L2; a prefill tile streams the blocks of one (sequence, KV head),
+// and tiles of the same (sequence, head) stream mostly the same blocks in the
+// same ascending order.  The slots are therefore taken in head-major order
+// ((head, sequence, tile)), cut into kXcds runs of equal total cost, and run
+// i is listed for XCD i (heaviest first inside each list), so that the CUs of
+// one XCD work on tiles of the same head and sequence at the same time and
+// their block streams meet in that XCD's L2 instead of each coming from the
+// last-level cache.  A workgroup takes from its own XCD's list first, then
+// from the others' once its own is exhausted.  sched: [0, 8) items per list,
+// [8, 16) next item to take, [16, 24) first list entry of each list.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+constexpr int kXcdBuckets = 1024;   // cost buckets per XCD list
+
+// XCD of the calling workgroup, from the hardware register (HW_REG_XCC_ID).
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & (kXcds - 1);
+}
+
+// Slot i = ((b * ntiles + tile) * H + h), nslots = nbt * H with nbt =
+// batch * ntiles; cost(i) > 0 for slots to run, cost <= maxcost.  hist: LDS
+// of kXcds * kXcdBuckets ints.
+template <class Cost>
+__device__ void schedule_by_xcd(int nbt, int H, int maxcost, Cost cost, int32_t* list,
+                                int32_t* sched, int* hist) {
+  __shared__ int wsum[kSchedThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nslots = nbt * H;
+  int shift = 0;
+  while ((maxcost >> shift) >= kXcdBuckets) ++shift;
+  for (int i = tid; i < kXcds * kXcdBuckets; i += kSchedThreads) hist[i] = 0;
+  // each thread owns a contiguous run of the head-major order
+  const int per = (nslots + kSchedThreads - 1) / kSchedThreads;
+  const int k0 = min(nslots, tid * per), k1 = min(nslots, k0 + per);
+  auto slot_of = [&](int k) { return (k % nbt) * H + k / nbt; };
+  long long local = 0;
+  for (int k = k0; k < k1; ++k) local += max(0, cost(slot_of(k)));
+  // exclusive scan of the runs' costs (64-bit: a wave sums into 32 bits, the
+  // waves' totals into 64)
+  long long incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  __shared__ long long wsum64[kSchedThreads / 64];
+  if (lane == 63) wsum64[wave] = incl;
+  __syncthreads();
+  long long base = 0, total = 0;
+  for (int w = 0; w < kSchedThreads / 64; ++w) {
+    if (w < wave) base += wsum64[w];
+    total += wsum64[w];
+  }
+  base += incl - local;
+  const long long tot = max(1LL, total);
+  auto bin_of = [&](long long prefix, int c) {
+    // the run an item's midpoint falls in; 2 (prefix) + c < 2^63 always
+    const int x = (int)((2 * prefix + c) * kXcds / (2 * tot));
+    const int bucket = min(kXcdBuckets - 1, min(c, maxcost) >> shift);
+    return min(x, kXcds - 1) * kXcdBuckets + (kXcdBuckets - 1 - bucket);   // heaviest first
+  };
+  {
+    long long run = base;
+    for (int k = k0; k < k1; ++k) {
+      const int c = cost(slot_of(k));
+      if (c > 0) atomicAdd(&hist[bin_of(run, c)], 1);
+      run += max(0, c);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the histogram in place; list starts per XCD
+  const int m = kXcds * kXcdBuckets;
+  const int hper = m / kSchedThreads;                 // 8 entries per thread
+  int hl = 0;
+  for (int j = 0; j < hper; ++j) hl += hist[tid * hper + j];
+  int hi = hl;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(hi, off);
+    if (lane >= off) hi += y;
+  }
+  if (lane == 63) wsum[wave] = hi;
+  __syncthreads();
+  int hb = 0;
+  for (int w = 0; w < wave; ++w) hb += wsum[w];
+  int hrun = hb + hi - hl;
+  for (int j = 0; j < hper; ++j) {
+    const int idx = tid * hper + j;
+    if (idx % kXcdBuckets == 0) sched[16 + idx / kXcdBuckets] = hrun;
+    const int h = hist[idx];
+    hist[idx] = hrun;
+    hrun += h;
+  }
+  __syncthreads();
+  {
+    long long run = base;
+    for (int k = k0; k < k1; ++k) {
+      const int i = slot_of(k);
+      const int c = cost(i);
+      if (c > 0) list[atomicAdd(&hist[bin_of(run, c)], 1)] = i;
+      run += max(0, c);
+    }
+  }
+  __syncthreads();
+  if (tid < kXcds) {
+    // after the fill, hist[x * kXcdBuckets + last] holds the end of list x
+    sched[tid] = hist[tid * kXcdBuckets + kXcdBuckets - 1] - sched[16 + tid];
+    sched[8 + tid] = 0;
+  }
+}
+
+// Persistent loop helper for XCD-clustered lists: the next slot for this
+// workgroup (its own XCD's list first), or -1 when every list is exhausted
+// (uniform across the workgroup).
+__device__ __forceinline__ int take_slot_xcd(int32_t* sched, const int32_t* list, int xcd,
+                                             int* item_s) {
+  if (threadIdx.x == 0) {
+    int got = -1;
+    for (int j = 0; j < kXcds && got < 0; ++j) {
+      const int x = (xcd + j) & (kXcds - 1);
+      const int n = __atomic_load_n(&sched[x], __ATOMIC_RELAXED);
+      if (__atomic_load_n(&sched[8 + x], __ATOMIC_RELAXED) >= n) continue;
+      const int k = atomicAdd(&sched[8 + x], 1);
+      if (k < n) got = list[sched[16 + x] + k];
+    }
+    *item_s = got;
+  }
+  __syncthreads();
+  const int v = *item_s;
+  __syncthreads();
+  return v;
+}
+
 // Persistent loop helper: returns the next item index, or -1 when the list
 // is exhausted (uniform across the workgroup).
 __device__ __forceinline__ int take_item(int32_t* sched, int* item_s) {
@@ -425,9 +560,9 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
 constexpr int kRingHalf = 256;   // plan entries per half of the LDS ring
 
 __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams p) {
-  extern __shared__ int hist[];
-  const int nslots = p.rg.batch * p.ntiles * p.H_kv;
-  schedule_by_cost(nslots, p.nbmax, [&](int i) { return p.plan_cnt[i]; }, p.worklist, p.sched, hist);
+  __shared__ int hist[kXcds * kXcdBuckets];
+  schedule_by_xcd(p.rg.batch * p.ntiles, p.H_kv, p.nbmax, [&](int i) { return p.plan_cnt[i]; },
+                  p.worklist, p.sched, hist);
 }
 
 // ---------------------------------------------------------------------------
@@ -828,10 +963,11 @@ template <bool FP8, int NCT, int W>
 __global__ __launch_bounds__(64 * W) void attn_prefill3_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) PrefillLds3 lds;
   __shared__ int item_s;
+  const int xcd = xcd_id();
   for (;;) {
-    const int k = take_item(p.sched, &item_s);
-    if (k < 0) break;
-    attn_prefill3_tile<FP8, NCT, W>(p, p.worklist[k], lds);
+    const int slot = take_slot_xcd(p.sched, p.worklist, xcd, &item_s);
+    if (slot < 0) break;
+    attn_prefill3_tile<FP8, NCT, W>(p, slot, lds);
   }
 }
 
@@ -850,7 +986,7 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hi
                      (size_t)p.nbmax * sizeof(uint32_t), s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), (size_t)(p.nbmax + 1) * sizeof(int), s, p);
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)p.nwg), block(64 * waves);

@@ -153,6 +153,21 @@ def prefill_ragged(seed: int = 0, new=(1024, 4096, 8192, 16384),
                     init_blocks=1, local_blocks=4, seed=seed)
 
 
+def prefill_ragged_dense(seed: int = 0) -> Workload:
+    """The ragged prefill's first three sequences alone ({1024, 4096, 8192} new
+    tokens after {0, 2048, 0}): every token sees at most 64 blocks, so its
+    selection is every visible block -- dense causal attention."""
+    return replace(prefill_ragged(seed, new=(1024, 4096, 8192), cached=(0, 2048, 0)),
+                   name="prefill_3seq_13312tok_dense_causal")
+
+
+def prefill_ragged_sparse(seed: int = 0) -> Workload:
+    """The ragged prefill's last sequence alone (16384 new tokens after 16384
+    cached): 129..256 visible blocks per token, 64 selected."""
+    return replace(prefill_ragged(seed, new=(16384,), cached=(16384,)),
+                   name="prefill_1seq_16384tok_after_16384_topk64")
+
+
 def decode_fp8_long(seed: int = 0, batch: int = 16, ctx: int = 131072) -> Workload:
     """Long-context decode with scale-free FP8 e4m3 K/V (N(0, 0.5) clamped to
     the e4m3 range) and BF16 index-K: batch 16, context 131072 (1024 blocks),
@@ -176,6 +191,8 @@ WORKLOADS = {
     "decode_batch64": decode_batch64,
     "spec_decode": spec_decode,
     "prefill_ragged": prefill_ragged,
+    "prefill_ragged_dense": prefill_ragged_dense,
+    "prefill_ragged_sparse": prefill_ragged_sparse,
     "decode_fp8_long": decode_fp8_long,
     "decode_fp8_long_fp8ik": decode_fp8_long_fp8ik,
 }

@@ -230,8 +230,9 @@ int msa_attention_partitions(const msa_ragged* rg, int32_t num_q_heads,
                              int32_t num_partitions);
 
 /* Workspace bytes msa_attention_paged and msa_attention_paged_shared need
- * (partials for the split-K combine, and the union-tile plan of prefill and
- * of shared speculative steps).  Returns 0 on invalid arguments. */
+ * (split-K ready flags and partials, and the union-tile plan of
+ * prefill and of shared speculative steps).  Returns 0 on invalid
+ * arguments.  The workspace needs no initial contents. */
 size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t top_k,
                                      int32_t num_partitions);
@@ -261,7 +262,13 @@ size_t msa_attention_workspace_bytes(const msa_ragged* rg, int32_t num_q_heads,
  * num_partitions 0 = automatic, else 1 .. 64 (decode / speculative routes).
  * workspace     device, >= msa_attention_workspace_bytes(...) bytes.
  *
- * When more than one partition is used the call enqueues the combine itself.
+ * With more than one partition, each partition stores its partial result
+ * (as msa_splitk_combine takes them) and a ready flag in the workspace, and
+ * the group's last partition merges them in partition order inside the
+ * same launch (no separate combine launch).  Flags carry a tag of the call
+ * and the merging partition clears them, so the workspace needs no initial
+ * contents and no clearing between calls, and the call stays capturable in
+ * a HIP graph.  Two calls that overlap on one workspace race.
  * Errors: as msa_indexer_paged.  batch == 0 is a no-op.
  */
 int msa_attention_paged(void* output, const void* q, const int32_t* d_indices,
@@ -328,7 +335,9 @@ int msa_attention_paged_noalloc(void* output, const void* q, const int32_t* d_in
 
 /*
  * Split-K combine ("msa" page: partials keyed on the ragged global query
- * row; the shared combine writes the ragged output directly).
+ * row; the shared combine writes the ragged output directly).  The merge
+ * msa_attention_paged performs inside its kernel, as a call of its own for
+ * partials computed elsewhere.
  *
  * Partition pi of row r, query head g holds its own normalised output
  * o_pi = partial_o[pi][r][g][:] and the natural log of its softmax
