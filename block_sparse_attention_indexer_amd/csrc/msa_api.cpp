@@ -303,10 +303,22 @@ int plan_latent(int32_t batch, int32_t max_seq_length, int32_t num_heads, int32_
   return (int)std::min<int64_t>(np, kMaxPartitions);
 }
 
-size_t latent_ws(int32_t batch, int32_t max_seq_length, int32_t num_heads, int np) {
+// Split-K workspace of the latent kernel: ready flags (one per partition of
+// each (row slot, latent head, column group)), partial outputs and
+// log-sum-exps.
+size_t latent_groups(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                     int32_t num_latent_heads) {
+  return (size_t)batch * max_seq_length * num_latent_heads *
+         latent_col_groups(num_heads / num_latent_heads);
+}
+
+size_t latent_ws(int32_t batch, int32_t max_seq_length, int32_t num_heads,
+                 int32_t num_latent_heads, int np) {
   if (np <= 1 || batch == 0 || max_seq_length == 0) return 0;
   const size_t rows = (size_t)np * batch * max_seq_length * num_heads;
-  return align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
+  return align_up(latent_groups(batch, max_seq_length, num_heads, num_latent_heads) * np *
+                  sizeof(uint64_t)) +
+         align_up(rows * MSA_HEAD_DIM * sizeof(float)) + align_up(rows * sizeof(float));
 }
 
 int check_latent_leaf(const msa_latent_leaf* lf, int32_t num_latent_heads, int64_t need_entries) {
@@ -445,7 +457,7 @@ size_t msa_latent_workspace_bytes(int32_t batch, int32_t max_seq_length, int32_t
   const int np = msa_latent_partitions(batch, max_seq_length, num_heads, num_latent_heads, window,
                                        top_c, num_partitions);
   if (np < 1) return 0;
-  return latent_ws(batch, max_seq_length, num_heads, np);
+  return latent_ws(batch, max_seq_length, num_heads, num_latent_heads, np);
 }
 
 int msa_latent_attention_paged(void* output, const void* q, const int32_t* input_row_offsets,
@@ -482,7 +494,7 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
   const int np = plan_latent(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
                              num_partitions, cus);
   if (np < 1) return np;
-  const size_t need = latent_ws(batch, max_seq_length, num_heads, np);
+  const size_t need = latent_ws(batch, max_seq_length, num_heads, num_latent_heads, np);
   if (need && !workspace) return MSA_ERR_NULL;
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
   const int ncg = latent_col_groups(num_heads / num_latent_heads);
@@ -511,18 +523,20 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.out = static_cast<uint16_t*>(output);
   if (np > 1) {
+    // flags, partial outputs, partial log-sum-exps; the kernel's last
+    // partition of each group merges (no separate combine launch)
     const size_t rows = (size_t)np * p.rcap * num_heads;
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align_up(rows * MSA_HEAD_DIM * sizeof(float)));
+    char* w = static_cast<char*>(workspace);
+    p.ready = reinterpret_cast<uint64_t*>(w);
+    w += align_up(latent_groups(batch, max_seq_length, num_heads, num_latent_heads) * np *
+                  sizeof(uint64_t));
+    p.part_o = reinterpret_cast<float*>(w);
+    w += align_up(rows * MSA_HEAD_DIM * sizeof(float));
+    p.part_lse = reinterpret_cast<float*>(w);
+    p.epoch = next_epoch();
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_latent(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
-  if (np > 1) {
-    CombineParams c{p.part_o, p.part_lse, input_row_offsets, p.out, batch, max_seq_length, np,
-                    num_heads, p.rcap};
-    if (launch_combine(c, s) != hipSuccess) return MSA_ERR_LAUNCH;
-  }
   return MSA_OK;
 }
 

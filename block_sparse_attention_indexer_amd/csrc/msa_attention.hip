@@ -24,88 +24,9 @@
 
 #include "msa_common.h"
 #include "msa_kernels.h"
+#include "msa_splitk.h"
 
 namespace msa {
-
-constexpr int kXcdCount = 8;   // XCDs of the chip; workgroup i runs on XCD i mod 8
-
-// Workgroup index -> (partition, group).  One partition: the identity.
-// Several: groups go round the XCDs (group q on XCD q mod 8) and a group's
-// partitions sit np * 8 indices apart, all on the group's XCD.
-__device__ __forceinline__ void splitk_slot(int idx, int np, int* pi, int* grp) {
-  if (np == 1) {
-    *pi = 0;
-    *grp = idx;
-    return;
-  }
-  const int xcd = idx % kXcdCount, s = idx / kXcdCount;
-  *pi = s % np;
-  *grp = (s / np) * kXcdCount + xcd;
-}
-
-// Merge of one wave's split-K partials: out = sum_pi exp(lse_pi - M) o_pi /
-// sum_pi exp(lse_pi - M) over the np partitions, in partition order
-// (deterministic whichever partition merges); lse = -inf carries no weight.
-// The wave's nc valid columns are spread over all 64 lanes: L = 64 / ncp
-// lanes per column (ncp = nc rounded up to a power of two, at least 2), each
-// lane taking CH chunks of 4 consecutive dims, CH = 32 / L.  Partitions are
-// read KB = 32 / CH at a time, every load of a batch in flight together,
-// with a running maximum (the sums so far are rescaled when a batch raises
-// it).  col_row(c) / col_head(c): ragged row and query head of column c.
-template <int CH, class ColRow, class ColHead>
-__device__ void merge_partials(const AttnParams& p, int nc, ColRow col_row, ColHead col_head,
-                               bool poisoned) {
-  constexpr int L = 32 / CH;          // lanes per column
-  constexpr int KB = 32 / CH;         // partitions per batch: 32 loads of 16 bytes
-  const int lane = threadIdx.x & 63;
-  const int c = lane / L;
-  if (c >= nc) return;
-  const int d0 = (lane % L) * 4 * CH;
-  const size_t col = (size_t)col_row(c) * p.H_q + col_head(c);
-  const size_t pstride = (size_t)p.rcap * p.H_q;
-  f32x4 acc[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float den = 0.f, M = neg_inf();
-  for (int k0 = 0; k0 < p.np; k0 += KB) {
-    float lk[KB];
-    f32x4 v[KB][CH];
-#pragma unroll
-    for (int q = 0; q < KB; ++q) {
-      const int k = min(k0 + q, p.np - 1);   // past np: re-read the last one, weight 0
-      lk[q] = p.part_lse[(size_t)k * pstride + col];
-      const float* po = p.part_o + ((size_t)k * pstride + col) * kDim + d0;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) v[q][j] = *reinterpret_cast<const f32x4*>(po + 4 * j);
-    }
-    float mb = M;
-#pragma unroll
-    for (int q = 0; q < KB; ++q)
-      if (k0 + q < p.np) mb = fmaxf(mb, lk[q]);
-    if (mb != M) {
-      const float r = M == neg_inf() ? 0.f : __expf(M - mb);
-      den *= r;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) acc[j] *= r;
-      M = mb;
-    }
-#pragma unroll
-    for (int q = 0; q < KB; ++q) {
-      const float w = (k0 + q < p.np && lk[q] != neg_inf()) ? __expf(lk[q] - M) : 0.f;
-      if (w != 0.f) {
-        den += w;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) acc[j] += w * v[q][j];
-      }
-    }
-  }
-  const float dinv = poisoned ? __builtin_nanf("") : den > 0.f ? 1.f / den : 0.f;
-  uint16_t* op = p.out + col * kDim + d0;
-#pragma unroll
-  for (int j = 0; j < CH; ++j)
-    *reinterpret_cast<u32x2*>(op + 4 * j) =
-        u32x2{pack_bf16(acc[j][0] * dinv, acc[j][1] * dinv), pack_bf16(acc[j][2] * dinv, acc[j][3] * dinv)};
-}
 
 template <bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
@@ -409,23 +330,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     return;
   }
   // Split-K: store this partition's normalised partial and its log-sum-exp
-  // (natural log), keyed on the ragged row, then flag it ready; the group's
-  // last partition (np - 1) waits for the others' flags and merges.
-  //
-  // All partitions of a group run on one XCD, so its L2 is the point where
-  // they meet: partials are ordinary stores (the vector L1 writes through to
-  // L2) whose completion a wave waits for before it raises its flag; flags
-  // are set and polled with atomics, which execute at L2; the merger reads
-  // the partials with ordinary loads, which its L1 cannot serve from a stale
-  // line because no workgroup reads a partial before its merger does.  (A
-  // device-scope fence would instead write back and invalidate the whole L2,
-  // and coherent stores and loads would cross to memory behind the kernel's
-  // own streaming traffic.)  A flag holds the call's epoch (never 0, new for
-  // every call), so whatever a workspace held before never reads as ready;
-  // the merger clears the flags it read, so a replay of a captured call
-  // (same epoch) does not find them set either.  The merger only waits for
-  // workgroups of lower index on its own XCD, which the hardware dispatches
-  // before it, so the wait ends.
+  // (natural log), keyed on the ragged row; the group's last partition
+  // merges (msa_splitk.h: the exchange stays in the group's XCD).
   const size_t col = (size_t)qrow * p.H_q + hq;
   const size_t pstride = (size_t)p.rcap * p.H_q;
   if (col_ok) {
@@ -437,45 +343,19 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     }
     if (g == 0) p.part_lse[(size_t)pi * pstride + col] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
-  __syncthreads();                 // ... and every wave's
-  uint64_t* flags = p.ready + (size_t)grp * p.np;
-  if (pi != p.np - 1) {
-    if (threadIdx.x == 0)
-      __hip_atomic_exchange(flags + pi, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
+  bool poisoned = false;
   __shared__ int timed_out;
-  if (threadIdx.x < 64) {
-    // wave 0: lane k watches partition k's flag (np <= 64).  The wait is
-    // bounded (about a second) so that a broken invariant shows up as NaN
-    // output instead of a kernel that never ends.
-    const bool mine = (int)threadIdx.x < p.np - 1;
-    bool late = true;
-    for (int spin = 0; spin < (1 << 20); ++spin) {
-      const uint64_t f = mine ? __hip_atomic_fetch_or(flags + threadIdx.x, 0ull, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                              : p.epoch;
-      if (__builtin_amdgcn_ballot_w64(f != p.epoch) == 0) {
-        late = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    if (mine) __hip_atomic_exchange(flags + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) timed_out = late;
-  }
-  __syncthreads();
-  // this wave's valid columns: l16 < nc (columns are token-major)
+  if (!splitk_arrive(p.ready + (size_t)grp * p.np, pi, p.np, p.epoch, &poisoned, &timed_out)) return;
+  // each wave merges its own columns: l16 < nc (columns are token-major)
   const int nc = min(16, ntok * p.G);
   const int ncp = nc <= 2 ? 2 : nc <= 4 ? 4 : nc <= 8 ? 8 : 16;
   auto row_of = [&](int cc) { return r0 + tok0 + cc / p.G; };
   auto head_of = [&](int cc) { return h * p.G + cc % p.G; };
   switch (ncp) {
-    case 2: merge_partials<1>(p, nc, row_of, head_of, timed_out); break;
-    case 4: merge_partials<2>(p, nc, row_of, head_of, timed_out); break;
-    case 8: merge_partials<4>(p, nc, row_of, head_of, timed_out); break;
-    default: merge_partials<8>(p, nc, row_of, head_of, timed_out); break;
+    case 2: splitk_merge<1>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
+    case 4: splitk_merge<2>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
+    case 8: splitk_merge<4>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
+    default: splitk_merge<8>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
   }
 }
 
@@ -487,9 +367,7 @@ size_t attention_decode_lds_bytes(const AttnParams& p) {
 hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s) {
   const int ntok_groups = (p.rg.max_seq + p.tpw - 1) / p.tpw;
   const int ntgb = (ntok_groups + p.ntg - 1) / p.ntg;
-  // np > 1: groups padded to a whole round of the XCDs (see splitk_slot)
-  const size_t groups = (size_t)p.rg.batch * p.H_kv * ntgb;
-  const size_t nwg = p.np == 1 ? groups : (groups + kXcdCount - 1) / kXcdCount * kXcdCount * p.np;
+  const size_t nwg = splitk_workgroups((size_t)p.rg.batch * p.H_kv * ntgb, p.np);
   const size_t lds = attention_decode_lds_bytes(p);
   dim3 grid((unsigned)nwg), block(64 * p.ntg);
   if (fp8) hipLaunchKernelGGL(attn_decode_kernel<true>, grid, block, lds, s, p);

@@ -30,6 +30,8 @@ struct LatentParams {
   uint16_t* out;          // bf16 [R][H][128]
   float* part_o;          // [np][rcap][H][128]
   float* part_lse;        // [np][rcap][H]
+  uint64_t* ready;        // split-K ready flags [group][np] (msa_splitk.h)
+  uint64_t epoch;         // per call, never 0
 };
 
 // Most list slots (entries) one partition of a latent row may hold.

@@ -38,12 +38,15 @@
 //
 // The sink joins one wave's running softmax in partition 0 as one more
 // logit with no value (max = sink, sum = 1 before any entry), so neither the
-// merge nor the split-K combine needs anything extra.
+// merge of the four waves nor the split-K merge needs anything extra.  With
+// several partitions, the group's last partition merges their results in
+// the same launch (msa_splitk.h).
 #include <algorithm>
 
 #include "msa_common.h"
 #include "msa_kernels.h"
 #include "msa_latent.h"
+#include "msa_splitk.h"
 #include "msa_lds.h"
 
 namespace msa {
@@ -129,9 +132,12 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   const int lane = tid & 63, wave = uniform((int)(tid >> 6));
   const int l16 = lane & 15, g = lane >> 4;
 
-  int id = blockIdx.x;
-  const int pi = id % p.np;
-  id /= p.np;
+  // group = (row slot, latent head, column group); its np partitions share
+  // an XCD (msa_splitk.h)
+  int pi, id;
+  splitk_slot(blockIdx.x, p.np, &pi, &id);
+  if (id >= p.batch * p.max_seq * p.H_lat * p.ncg) return;   // padding of the last XCD round
+  const int grp = id;
   const int cg = id % p.ncg;
   id /= p.ncg;
   const int hl = id % p.H_lat;
@@ -478,44 +484,56 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     }
   }
   __syncthreads();
-  if (wave >= NCT) return;
-  const int ct = wave;
-  if (!col_ok[ct]) return;
-  float mw[kLatWaves], M = neg_inf();
+  // waves 0 .. NCT - 1 each merge the four waves' states of one column tile
+  const int ct = min(wave, NCT - 1);
+  if (wave < NCT && col_ok[ct]) {
+    float mw[kLatWaves], M = neg_inf();
 #pragma unroll
-  for (int w = 0; w < kLatWaves; ++w) {
-    mw[w] = stat[((w * NCT + ct) * 2 + 0) * 16 + l16];
-    M = fmaxf(M, mw[w]);
-  }
-  float lsum = 0.f;
-  f32x4 o[8];
+    for (int w = 0; w < kLatWaves; ++w) {
+      mw[w] = stat[((w * NCT + ct) * 2 + 0) * 16 + l16];
+      M = fmaxf(M, mw[w]);
+    }
+    float lsum = 0.f;
+    f32x4 o[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < kLatWaves; ++w) {
-    const float sw = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
-    lsum += sw * stat[((w * NCT + ct) * 2 + 1) * 16 + l16];
-    const f32x4* src = reinterpret_cast<const f32x4*>(L.ring[w]);
+    for (int w = 0; w < kLatWaves; ++w) {
+      const float sw = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
+      lsum += sw * stat[((w * NCT + ct) * 2 + 1) * 16 + l16];
+      const f32x4* src = reinterpret_cast<const f32x4*>(L.ring[w]);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] += sw * src[(ct * 8 + dt) * 64 + lane];
-  }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      for (int dt = 0; dt < 8; ++dt) o[dt] += sw * src[(ct * 8 + dt) * 64 + lane];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 
-  // ---- store: O^T tile dt, C row 4g + i is dim 16dt + 4g + i ----------------------
-  const size_t hrow = (size_t)r * p.H + hl * p.G + cg * 64 + 16 * ct + l16;
-  if (p.np == 1) {
-    uint16_t* op = p.out + hrow * kDim + 4 * g;
+    // ---- store: O^T tile dt, C row 4g + i is dim 16dt + 4g + i --------------------
+    const size_t hrow = (size_t)r * p.H + hl * p.G + cg * 64 + 16 * ct + l16;
+    if (p.np == 1) {
+      uint16_t* op = p.out + hrow * kDim + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<u32x2*>(op + 16 * dt) =
-          u32x2{pack_bf16(o[dt][0] * inv, o[dt][1] * inv), pack_bf16(o[dt][2] * inv, o[dt][3] * inv)};
-  } else {
-    const size_t prow = (size_t)pi * p.rcap * p.H + hrow;
-    float* op = p.part_o + prow * kDim + 4 * g;
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<u32x2*>(op + 16 * dt) =
+            u32x2{pack_bf16(o[dt][0] * inv, o[dt][1] * inv), pack_bf16(o[dt][2] * inv, o[dt][3] * inv)};
+    } else {
+      const size_t prow = (size_t)pi * p.rcap * p.H + hrow;
+      float* op = p.part_o + prow * kDim + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt) = o[dt] * inv;
-    if (g == 0) p.part_lse[prow] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : neg_inf();
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt) = o[dt] * inv;
+      if (g == 0) p.part_lse[prow] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : neg_inf();
+    }
   }
+  if (p.np == 1) return;
+  // split-K: the group's last partition merges the partials of its (up to)
+  // 64 query heads, 4 threads per head
+  bool poisoned = false;
+  // (the wave-merge statistics are dead past the arrival's first barrier)
+  if (!splitk_arrive(p.ready + (size_t)grp * p.np, pi, p.np, p.epoch, &poisoned,
+                     reinterpret_cast<int*>(stat)))
+    return;
+  const int nc = min(64, p.G - cg * 64);
+  splitk_merge<8>(p.part_o, p.part_lse, p.out, p.H, p.rcap, p.np, nc, [&](int) { return r; },
+                  [&](int c) { return hl * p.G + cg * 64 + c; }, tid, poisoned);
 }
 
 template <bool FP8>
@@ -527,7 +545,7 @@ static void launch_latent_t(const LatentParams& p, dim3 grid, dim3 block, hipStr
 }
 
 hipError_t launch_latent(const LatentParams& p, hipStream_t s) {
-  const size_t nwg = (size_t)p.batch * p.max_seq * p.H_lat * p.ncg * p.np;
+  const size_t nwg = splitk_workgroups((size_t)p.batch * p.max_seq * p.H_lat * p.ncg, p.np);
   const dim3 grid((unsigned)nwg), block(64 * kLatWaves);
   if (p.fp8) launch_latent_t<true>(p, grid, block, s);
   else launch_latent_t<false>(p, grid, block, s);

@@ -439,7 +439,9 @@ size_t msa_latent_workspace_bytes(int32_t batch, int32_t max_seq_length, int32_t
  *
  * Errors: MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_PARAM, MSA_ERR_DTYPE,
  * MSA_ERR_WORKSPACE, MSA_ERR_LAUNCH, MSA_ERR_DEVICE.  batch == 0 is a no-op.
- * When more than one partition is used the call enqueues the combine itself.
+ * With more than one partition, the last partition of each (row, latent
+ * head, group of 64 query heads) merges the partitions' results inside the
+ * same launch (no combine launch); the workspace needs no initial contents.
  */
 int msa_latent_attention_paged(void* output, const void* q, const int32_t* input_row_offsets,
                                int32_t batch, int32_t max_seq_length,
