@@ -27,6 +27,8 @@ MSA_MAX_BLOCKS = 8192     # most blocks one sequence may hold
 MSA_MAX_TOPK = 512        # largest top_k
 MSA_MAX_KV_HEADS = 256    # most KV heads of one call
 MSA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # msa_attention_paged_noalloc's fixed workspace
+MSA_DEVERR_PAGE = 1       # device error word: a page id outside the pool
+MSA_DEVERR_LENGTH = 2     # device error word: a length beyond the bounds or the table
 
 
 class MsaError(RuntimeError):
@@ -108,6 +110,7 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(PagedCache),
         ctypes.POINTER(PagedCache), ctypes.POINTER(Ragged), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]),
+    "msa_device_errors": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int, ctypes.c_void_p]),
     "msa_latent_partitions": (ctypes.c_int, [ctypes.c_int32] * 7),
     "msa_latent_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 7),
     "msa_latent_attention_paged": (ctypes.c_int, [
@@ -302,6 +305,15 @@ def msa_attention_paged_noalloc(output, q, d_indices, k_cache, v_cache, rg: Ragg
                                                float(scale), num_partitions, _stream(stream))
     _check(st, "msa_attention_paged_noalloc")
     return output
+
+
+def msa_device_errors(clear: bool = True, stream=None) -> int:
+    """The device error word (MSA_DEVERR_* bits of bad table data met since
+    the last clear), read after the stream's work so far; clears it."""
+    bits = ctypes.c_uint32(0)
+    st = library().msa_device_errors(ctypes.byref(bits), 1 if clear else 0, _stream(stream))
+    _check(st, "msa_device_errors")
+    return int(bits.value)
 
 
 def msa_splitk_combine(output, partial_o, partial_lse, input_row_offsets, batch: int,

@@ -23,7 +23,7 @@ LIB = os.path.join(LIBDIR, "libmsa.so")
 ARCH = "gfx950"
 
 SOURCES = ["msa_indexer.hip", "msa_attention.hip", "msa_prefill.hip", "msa_latent.hip",
-           "msa_noalloc.hip", "msa_api.cpp"]
+           "msa_noalloc.hip", "msa_errors.hip", "msa_api.cpp"]
 
 # Packed-FP32 VALU ops are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

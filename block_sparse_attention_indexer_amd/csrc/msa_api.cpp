@@ -21,6 +21,9 @@ namespace {
 
 using namespace msa;
 
+static_assert(kErrPage == MSA_DEVERR_PAGE && kErrLength == MSA_DEVERR_LENGTH,
+              "device error bits match the header");
+
 constexpr size_t kAlign = 256;
 constexpr int kMaxPartitions = 64;
 constexpr int kMaxDevices = 64;
@@ -398,6 +401,7 @@ int msa_indexer_paged(int32_t* d_indices, const void* q_idx, const msa_paged_cac
   p.top_k = top_k;
   p.init = init_blocks;
   p.local = local_blocks;
+  p.err = device_error_word();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.nbmax > top_k) {
     hipError_t e;
@@ -522,6 +526,7 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
   p.rcap = batch * max_seq_length;
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.out = static_cast<uint16_t*>(output);
+  p.err = device_error_word();
   if (np > 1) {
     // flags, partial outputs, partial log-sum-exps; the kernel's last
     // partition of each group merges (no separate combine launch)
@@ -619,6 +624,7 @@ int attention_paged_entry(void* output, const void* q, const int32_t* d_indices,
   p.nbmax = block_bound(*rg);
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.out = static_cast<uint16_t*>(output);
+  p.err = device_error_word();
   const bool fp8 = k_cache->dtype == MSA_DTYPE_FP8_E4M3;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (union_tiles) {

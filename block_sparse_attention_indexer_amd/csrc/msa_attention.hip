@@ -54,6 +54,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   const int r0 = p.rg.offs[b];
   const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);   // keeps rows < rcap
   const int c = p.rg.clen[b];
+  // more new tokens than the host bound, or blocks past the table (clipped)
+  if (threadIdx.x == 0 && pi == 0 && tgb == 0 && h == 0 &&
+      (p.rg.offs[b + 1] - r0 > p.rg.max_seq || (n > 0 && (c + n - 1) / kBlock >= p.nbmax)))
+    report_error(p.err, kErrLength);
   const int tok0 = (tgb * W + wave) * p.tpw;
   const int ntok = max(0, min(n - tok0, p.tpw));
 
@@ -166,6 +170,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
       mk_lane = umk[e_lo + s0 + lane];
       const int pg = p.rg.table[(size_t)b * p.rg.stride + blk_lane];
       pg_lane = (unsigned)pg < (unsigned)p.k.num_pages ? pg : -1;   // bad ids: block skipped
+      if (pg_lane < 0) report_error(p.err, kErrPage);
     }
 
     // Addresses = wave-uniform base (page, head, half block, row constant)

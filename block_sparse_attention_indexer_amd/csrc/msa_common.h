@@ -105,6 +105,12 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Records `bit` (kErrPage, kErrLength) in the device error word (rare paths
+// only; null: not reported).
+__device__ __forceinline__ void report_error(uint32_t* err, uint32_t bit) {
+  if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // 2^x with the hardware instruction (v_exp_f32): exact at 0, 0 at -inf,
 // ~1 ulp elsewhere; results below the normal range flush to 0, which only
 // affects probabilities under 2^-126.

@@ -179,7 +179,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
     // page 0 and write no score
     int pg_lane = 0;
     if (lane < nblk) pg_lane = p.rg.table[(size_t)b * p.rg.stride + blk_lo + lane];
-    if ((unsigned)pg_lane >= (unsigned)p.ik.num_pages) pg_lane = -1;
+    if ((unsigned)pg_lane >= (unsigned)p.ik.num_pages) {
+      pg_lane = -1;
+      if (lane < nblk) report_error(p.err, kErrPage);
+    }
     const char* head_base = pool + (size_t)hk * p.ik.head_stride * ESZ + lane_off;
     const float* scale_head = FP8 ? p.ik.scale + (size_t)hk * p.ik.scale_head_stride : nullptr;
 

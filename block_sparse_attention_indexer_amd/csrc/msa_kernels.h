@@ -11,6 +11,11 @@ struct msa_ragged;
 
 namespace msa {
 
+// Bits of the per-device error word (the values of msa.h's MSA_DEVERR_*):
+// bad table data that a kernel met, skipped or clipped.
+constexpr uint32_t kErrPage = 1u;     // a page id outside the pool
+constexpr uint32_t kErrLength = 2u;   // a length beyond the host bounds or the table
+
 // A paged cache as the kernels see it: base pointer and element strides,
 // plus the per-token scales of an FP8 index-K cache (null otherwise).
 struct Pool {
@@ -46,6 +51,7 @@ struct IndexerParams {
   int32_t* sched;         // [0] items in the list, [1] next item to take
   int32_t H_kv, H_ik;
   int32_t top_k, init, local;
+  uint32_t* err;          // device error word (bad table data), or null
 };
 
 struct AttnParams {
@@ -77,6 +83,7 @@ struct AttnParams {
   int32_t* worklist;      // [B * ntiles * H_kv] non-empty plan slots, one list per XCD
   int32_t* sched;         // kSchedInts: per XCD list, its length, next entry and start
   int32_t nwg;            // persistent workgroups launched
+  uint32_t* err;          // device error word (bad table data), or null
 };
 
 struct CombineParams {
@@ -112,6 +119,10 @@ void prefill_tiling(int G, bool fp8, int waves, int* tq, int* nct);
 
 // Bytes of LDS the decode attention kernel needs per workgroup.
 size_t attention_decode_lds_bytes(const AttnParams& p);
+
+// Device address of the current device's error word (msa_errors.hip), or
+// null if it cannot be resolved.
+uint32_t* device_error_word();
 
 // The body of the attention entry points (validation, plan, launches) with
 // the workspace given; `shared` picks the union-tile kernel for speculative

@@ -32,6 +32,7 @@ struct LatentParams {
   float* part_lse;        // [np][rcap][H]
   uint64_t* ready;        // split-K ready flags [group][np] (msa_splitk.h)
   uint64_t epoch;         // per call, never 0
+  uint32_t* err;          // device error word (bad table data), or null
 };
 
 // Most list slots (entries) one partition of a latent row may hold.

@@ -158,6 +158,10 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   // checked that the window leaf's table covers max_seq new positions more)
   const int swa_len = p.window > 0 ? min(p.swa.clen[b], tab_cap(p.swa.stride) - p.max_seq) : 0;
   const int comp_len = p.top_c > 0 ? min(p.comp.clen[b], tab_cap(p.comp.stride)) : 0;
+  if (threadIdx.x == 0 && pi == 0 && hl == 0 && cg == 0 && t == 0 &&
+      ((p.window > 0 && swa_len < p.swa.clen[b]) || (p.top_c > 0 && comp_len < p.comp.clen[b]) ||
+       r1 - r0 > p.max_seq))
+    report_error(p.err, kErrLength);
   if (t >= min(r1 - r0, p.max_seq)) return;
   const int r = r0 + t;
 
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
       ent[k] = (v & m) | ((s < n_swa ? lo + s : -1) & ~m);
     }
     int pg[kPer];
+    bool att[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int s = s0 + tid + 64 * kLatWaves * k;
@@ -212,6 +217,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
       const int v = *(win ? swa_tab + (e >> 7) : cmp ? comp_tab + (e >> 7) : p.offs);
       const int m = -(int)(win || cmp);
       pg[k] = (v & m) | ~m;
+      att[k] = win || cmp;
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -222,6 +228,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
         // a page id outside the pool (bad table data) is skipped like an
         // invalid entry, so no read leaves the pool
         const int npages = s < n_swa ? p.swa.pool.num_pages : p.comp.pool.num_pages;
+        if (att[k] && (unsigned)pg[k] >= (unsigned)npages) report_error(p.err, kErrPage);
         if ((unsigned)pg[k] < (unsigned)npages)
           a = s < n_swa ? swa_base + (size_t)pg[k] * p.swa.pool.page_stride * ESZ +
                               (size_t)(ent[k] & 127) * p.swa.pool.token_stride * ESZ

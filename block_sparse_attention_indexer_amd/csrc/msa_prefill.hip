@@ -355,7 +355,10 @@ __device__ void indexer_prefill_tile(const IndexerParams& p, const IdxTile& T, c
   }
   auto stage = [&](int rel, int buf) {
     int pg = pages_lds[rel];
-    if ((unsigned)pg >= (unsigned)npages) pg = 0;
+    if ((unsigned)pg >= (unsigned)npages) {
+      pg = 0;
+      if (lane == 0) report_error(p.err, kErrPage);
+    }
     const char* kb = pool + (size_t)pg * page_bytes + head_bytes;
     char* st = ring + buf * STAGE;
 #pragma unroll
@@ -514,6 +517,10 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
   const int c = p.rg.clen[b];
   const int ntok = min(p.tq, n - t0);
   const int nb_last = min((c + t0 + ntok - 1) / kBlock + 1, p.nbmax);
+  // more new tokens than the host bound, or blocks past the table (clipped)
+  if (lane == 0 && h == 0 &&
+      ((tile == 0 && p.rg.offs[b + 1] - r0 > p.rg.max_seq) || (c + t0 + ntok - 1) / kBlock >= p.nbmax))
+    report_error(p.err, kErrLength);
   for (int i = lane; i < nb_last; i += 64) member[i] = 0u;
   __syncthreads();
   for (int tl = 0; tl < ntok; ++tl) {
@@ -539,6 +546,7 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
       const int pg = trow[i];
       ids[pos] = i;
       pgs[pos] = (unsigned)pg < (unsigned)p.k.num_pages ? pg : -1;
+      if ((unsigned)pg >= (unsigned)p.k.num_pages) report_error(p.err, kErrPage);
       msk[pos] = m;
     }
     cnt += __popcll(bal);

@@ -148,6 +148,32 @@ typedef struct msa_ragged {
 } msa_ragged;
 
 /* ------------------------------------------------------------------------ */
+/* Bad device data                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* The kernels never read outside the caller's buffers, whatever the device
+ * data holds: a page id outside [0, num_pages) skips its block (or stands
+ * in page 0 for it), and per-sequence new-token counts or lengths beyond
+ * what max_seq_length and the lookup table allow are clipped.  The result
+ * of the sequence concerned is then undefined; every other sequence's is
+ * exact.  Such data also sets bits in a per-device error word: */
+enum {
+    MSA_DEVERR_PAGE = 1,     /* a lookup-table page id outside the pool       */
+    MSA_DEVERR_LENGTH = 2    /* a new-token count above max_seq_length, or a   */
+                             /* sequence longer than its lookup-table row      */
+};
+
+/*
+ * Reads the current device's error word into *bits after everything
+ * enqueued on `stream` so far has run, and with clear != 0 resets it to 0.
+ * Synchronises the stream (a diagnostic call, not for graph capture).  The
+ * word collects bits from every call on the device since the last clear.
+ *
+ * Errors: MSA_ERR_NULL (bits), MSA_ERR_DEVICE, MSA_ERR_LAUNCH.
+ */
+int msa_device_errors(uint32_t* bits, int clear, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Indexer                                                                  */
 /* ------------------------------------------------------------------------ */
 

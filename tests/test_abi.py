@@ -25,7 +25,7 @@ def test_library_exports_every_declared_function():
 def test_binding_constants_match_header():
     text = open(B.HEADER).read()
     for name in ("MSA_MAX_SPEC_DRAFT", "MSA_MAX_BLOCKS", "MSA_MAX_TOPK", "MSA_MAX_KV_HEADS",
-                 "MSA_DTYPE_BF16",
+                 "MSA_DEVERR_PAGE", "MSA_DEVERR_LENGTH", "MSA_DTYPE_BF16",
                  "MSA_DTYPE_FP8_E4M3", "MSA_LATENT_MAX_TOPC"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m, name
@@ -165,6 +165,10 @@ def test_attention_validation(entry):
     need = B.msa_attention_workspace_bytes(rg(), 64, 8, 16, 4)
     assert attention(rg(), k, v, np_=4, ws=need - 1) == WORKSPACE
     assert attention(rg(batch=0), k, v) == OK
+
+
+def test_device_errors_validation():
+    assert B.library().msa_device_errors(None, 1, None) == NULL
 
 
 def noalloc(r, k, v, hq=64, hkv=8, top_k=16, np_=0, scale=0.1):

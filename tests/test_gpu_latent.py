@@ -196,7 +196,9 @@ def test_page_ids_outside_the_pool_are_skipped():
     bad = {0: 2, 1: 1}                      # sequence -> logical page made bad
     inp.comp_lookup_table[0, bad[0]] = P + 1000
     inp.comp_lookup_table[1, bad[1]] = -7
+    B.msa_device_errors(clear=True)
     got = B.run_latent(inp, num_partitions=2).clone()
+    assert B.msa_device_errors() == B.MSA_DEVERR_PAGE
     offs = inp.input_row_offsets.cpu().tolist()
     for b, lp in bad.items():
         rows = lists[offs[b]:offs[b + 1]]
@@ -216,9 +218,12 @@ def test_lengths_past_the_lookup_table_stay_inside_it():
     w = wl("lat_badlen", [1, 2, 1], [700, 300, 1200], [900, 500, 300], H=16, window=64, top_c=120,
            seed=32)
     inp = LI.make_latent_inputs(w, DEV)
+    B.msa_device_errors(clear=True)
     clean = B.run_latent(inp, num_partitions=2).clone()
+    assert B.msa_device_errors() == 0
     inp.swa_cache_lengths[0] = 10 ** 9
     inp.comp_cache_lengths[0] = 10 ** 9
     got = B.run_latent(inp, num_partitions=2)
     torch.cuda.synchronize()
+    assert B.msa_device_errors() == B.MSA_DEVERR_LENGTH
     assert torch.equal(got[1:], clean[1:])

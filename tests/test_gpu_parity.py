@@ -225,14 +225,17 @@ def test_bad_page_ids_stay_inside_their_sequence(route):
     wl = wl_custom(f"badpage_{route}", new, [3000, 5000, 700], top_k=6)
     say(f"[case] {wl.name}")
     inp = I.make_inputs(wl, DEV)
+    B.msa_device_errors(clear=True)
     d0 = B.run_indexer(inp).clone()
     o0 = B.run_attention(inp, d0, shared=shared).clone()
+    assert B.msa_device_errors() == 0             # clean data reports nothing
     P = inp.k_cache.shape[0]
     inp.kv_lookup_table[0, 3] = P + 50
     inp.kv_lookup_table[0, 10] = -3
     d1 = B.run_indexer(inp)
     o1 = B.run_attention(inp, d1, shared=shared)
     torch.cuda.synchronize()
+    assert B.msa_device_errors() == B.MSA_DEVERR_PAGE   # ... and the bad ids are reported
     r1 = int(inp.input_row_offsets[1])
     assert torch.equal(d0[r1:], d1[r1:])
     assert torch.equal(o0[r1:].view(torch.int16), o1[r1:].view(torch.int16))
@@ -263,11 +266,14 @@ def test_lengths_past_the_lookup_table_stay_inside_it(route):
                   wl.top_k, wl.softmax_scale)
         return d, out
 
+    B.msa_device_errors(clear=True)
     d_tight = B.run_indexer(inp).clone()
     d0, o0 = step()
+    assert B.msa_device_errors() == 0             # the loose host bound is not an error
     inp.cache_lengths[-1] = 10 ** 6
     d1, o1 = step()
     torch.cuda.synchronize()
+    assert B.msa_device_errors() & B.MSA_DEVERR_LENGTH
     assert torch.equal(d0, d_tight)              # the loose host bound changes nothing
     rl = int(inp.input_row_offsets[-2])
     assert torch.equal(d0[:rl], d1[:rl])
