@@ -306,6 +306,32 @@ int plan_latent(int32_t batch, int32_t max_seq_length, int32_t num_heads, int32_
   return (int)std::min<int64_t>(np, kMaxPartitions);
 }
 
+// Leaves of two storage types: the window leaf's tiles and the list's go
+// through two launches (one tile format each) as disjoint partition sets of
+// one split-K, np_swa partitions for the window positions and np_comp for
+// the list slots, in proportion to their tiles, each at least one and
+// enough that a partition's entries fit the kernel's LDS list.
+void latent_split(int32_t window, int32_t top_c, int np, int* np_swa, int* np_comp) {
+  const int64_t ta = std::max<int64_t>(1, ((int64_t)window + kLatentTile - 1) / kLatentTile);
+  const int64_t tb = std::max<int64_t>(1, ((int64_t)top_c + kLatentTile - 1) / kLatentTile);
+  const int64_t per_max = kLatentMaxSlots / kLatentTile;
+  const int64_t need_a = (ta + per_max - 1) / per_max, need_b = (tb + per_max - 1) / per_max;
+  const int64_t total = std::max<int64_t>(std::max<int64_t>(np, 2), need_a + need_b);
+  int64_t a = (total * ta + (ta + tb) / 2) / (ta + tb);
+  a = std::max(need_a, std::min(a, total - need_b));
+  *np_swa = (int)a;
+  *np_comp = (int)(total - a);
+}
+
+// Partitions of a call: both leaves read -> the two-type split's total
+// (also what the size query reserves, since it does not know the types).
+int latent_total_partitions(int32_t window, int32_t top_c, int np) {
+  if (window <= 0 || top_c <= 0) return np;
+  int a = 0, b = 0;
+  latent_split(window, top_c, np, &a, &b);
+  return std::max(np, a + b);
+}
+
 // Split-K workspace of the latent kernel: ready flags (one per partition of
 // each (row slot, latent head, column group)), partial outputs and
 // log-sum-exps.
@@ -461,7 +487,8 @@ size_t msa_latent_workspace_bytes(int32_t batch, int32_t max_seq_length, int32_t
   const int np = msa_latent_partitions(batch, max_seq_length, num_heads, num_latent_heads, window,
                                        top_c, num_partitions);
   if (np < 1) return 0;
-  return latent_ws(batch, max_seq_length, num_heads, num_latent_heads, np);
+  return latent_ws(batch, max_seq_length, num_heads, num_latent_heads,
+                   latent_total_partitions(window, top_c, np));
 }
 
 int msa_latent_attention_paged(void* output, const void* q, const int32_t* input_row_offsets,
@@ -488,21 +515,26 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
     if (!comp || !comp_indices) return MSA_ERR_NULL;
     if ((st = check_latent_leaf(comp, num_latent_heads, comp->max_cache_length)) != MSA_OK) return st;
   }
-  // one tile format per call: the leaves that are read share their type
+  // Leaves of one storage type take one launch; leaves of two types take
+  // one launch per leaf (one tile format each) as disjoint partition sets
+  // of one split-K, merged by the list launch's last partition.
+  const bool mixed = window > 0 && top_c > 0 && comp->cache.dtype != swa->cache.dtype;
   const int leaf_dtype = window > 0 ? swa->cache.dtype
                          : top_c > 0 ? comp->cache.dtype
                                      : (int)MSA_DTYPE_BF16;
-  if (window > 0 && top_c > 0 && comp->cache.dtype != swa->cache.dtype) return MSA_ERR_DTYPE;
   int cus = 0;
   if (num_partitions == 0 && (st = current_device(&cus)) != MSA_OK) return st;
   const int np = plan_latent(batch, max_seq_length, num_heads, num_latent_heads, window, top_c,
                              num_partitions, cus);
   if (np < 1) return np;
-  const size_t need = latent_ws(batch, max_seq_length, num_heads, num_latent_heads, np);
+  int np_swa = 0, np_comp = 0;
+  if (mixed) latent_split(window, top_c, np, &np_swa, &np_comp);
+  const int np_total = mixed ? np_swa + np_comp : np;
+  const size_t need = latent_ws(batch, max_seq_length, num_heads, num_latent_heads, np_total);
   if (need && !workspace) return MSA_ERR_NULL;
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE;
   const int ncg = latent_col_groups(num_heads / num_latent_heads);
-  if ((int64_t)batch * max_seq_length * num_latent_heads * ncg * np > (int64_t)INT32_MAX)
+  if ((int64_t)batch * max_seq_length * num_latent_heads * ncg * np_total > (int64_t)INT32_MAX)
     return MSA_ERR_SHAPE;
   if (num_partitions != 0 && (st = current_device(&cus)) != MSA_OK) return st;
 
@@ -523,17 +555,19 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
   p.ncg = ncg;
   p.window = window;
   p.np = np;
+  p.pi_base = 0;
+  p.np_total = np_total;
   p.rcap = batch * max_seq_length;
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.out = static_cast<uint16_t*>(output);
   p.err = device_error_word();
-  if (np > 1) {
+  if (np_total > 1) {
     // flags, partial outputs, partial log-sum-exps; the kernel's last
     // partition of each group merges (no separate combine launch)
-    const size_t rows = (size_t)np * p.rcap * num_heads;
+    const size_t rows = (size_t)np_total * p.rcap * num_heads;
     char* w = static_cast<char*>(workspace);
     p.ready = reinterpret_cast<uint64_t*>(w);
-    w += align_up(latent_groups(batch, max_seq_length, num_heads, num_latent_heads) * np *
+    w += align_up(latent_groups(batch, max_seq_length, num_heads, num_latent_heads) * np_total *
                   sizeof(uint64_t));
     p.part_o = reinterpret_cast<float*>(w);
     w += align_up(rows * MSA_HEAD_DIM * sizeof(float));
@@ -541,7 +575,23 @@ int msa_latent_attention_paged(void* output, const void* q, const int32_t* input
     p.epoch = next_epoch();
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_latent(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  if (!mixed) {
+    if (launch_latent(p, s) != hipSuccess) return MSA_ERR_LAUNCH;
+    return MSA_OK;
+  }
+  // the window leaf's partitions (the row's first ones, holding the sink) ...
+  LatentParams a = p;
+  a.top_c = 0;
+  a.np = np_swa;
+  a.fp8 = swa->cache.dtype == MSA_DTYPE_FP8_E4M3;
+  if (launch_latent(a, s) != hipSuccess) return MSA_ERR_LAUNCH;
+  // ... then the list's, whose last partition merges all of them
+  LatentParams c = p;
+  c.window = 0;
+  c.np = np_comp;
+  c.pi_base = np_swa;
+  c.fp8 = comp->cache.dtype == MSA_DTYPE_FP8_E4M3;
+  if (launch_latent(c, s) != hipSuccess) return MSA_ERR_LAUNCH;
   return MSA_OK;
 }
 

@@ -22,10 +22,12 @@ struct LatentParams {
   int32_t top_c;
   const float* sink;      // [H]
   LatentLeaf swa, comp;
-  int32_t fp8;            // 1: both leaves FP8 e4m3 (scale-free), 0: both BF16
+  int32_t fp8;            // 1: the leaves this launch reads are FP8 e4m3 (scale-free), 0: BF16
   int32_t H, H_lat, G;    // query heads, latent heads, query heads per latent head
   int32_t ncg;            // column groups of 64 query heads per latent head
-  int32_t window, np, rcap;
+  int32_t window, np, rcap;  // np: partitions of this launch
+  int32_t pi_base;        // index of this launch's first partition among the row's
+  int32_t np_total;       // partitions of the row over every launch of the call
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* out;          // bf16 [R][H][128]
   float* part_o;          // [np][rcap][H][128]

@@ -36,7 +36,7 @@
 // bytes are finite; for FP8 leaves they could decode as NaN, so the wave
 // zeroes such rows of its tile before reading it.
 //
-// The sink joins one wave's running softmax in partition 0 as one more
+// The sink joins one wave's running softmax in the row's partition 0 as one more
 // logit with no value (max = sink, sum = 1 before any entry), so neither the
 // merge of the four waves nor the split-K merge needs anything extra.  With
 // several partitions, the group's last partition merges their results in
@@ -138,6 +138,10 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   splitk_slot(blockIdx.x, p.np, &pi, &id);
   if (id >= p.batch * p.max_seq * p.H_lat * p.ncg) return;   // padding of the last XCD round
   const int grp = id;
+  // this partition among all of the row's (with leaves of two storage
+  // types, the window leaf's partitions come from one launch, the list's
+  // from a second one)
+  const int gpi = p.pi_base + pi;
   const int cg = id % p.ncg;
   id /= p.ncg;
   const int hl = id % p.H_lat;
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
     for (int dt = 0; dt < 8; ++dt) O[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[ct] = neg_inf();
     l_run[ct] = 0.f;
-    if (pi == 0 && wave == 0 && col_ok[ct]) {
+    if (gpi == 0 && wave == 0 && col_ok[ct]) {
       const float sk = sink_v[ct];
       if (sk != neg_inf()) {
         m_run[ct] = sk * kLog2e;
@@ -516,30 +520,30 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
 
     // ---- store: O^T tile dt, C row 4g + i is dim 16dt + 4g + i --------------------
     const size_t hrow = (size_t)r * p.H + hl * p.G + cg * 64 + 16 * ct + l16;
-    if (p.np == 1) {
+    if (p.np_total == 1) {
       uint16_t* op = p.out + hrow * kDim + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         *reinterpret_cast<u32x2*>(op + 16 * dt) =
             u32x2{pack_bf16(o[dt][0] * inv, o[dt][1] * inv), pack_bf16(o[dt][2] * inv, o[dt][3] * inv)};
     } else {
-      const size_t prow = (size_t)pi * p.rcap * p.H + hrow;
+      const size_t prow = (size_t)gpi * p.rcap * p.H + hrow;
       float* op = p.part_o + prow * kDim + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt) = o[dt] * inv;
       if (g == 0) p.part_lse[prow] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : neg_inf();
     }
   }
-  if (p.np == 1) return;
+  if (p.np_total == 1) return;
   // split-K: the group's last partition merges the partials of its (up to)
   // 64 query heads, 4 threads per head
   bool poisoned = false;
   // (the wave-merge statistics are dead past the arrival's first barrier)
-  if (!splitk_arrive(p.ready + (size_t)grp * p.np, pi, p.np, p.epoch, &poisoned,
+  if (!splitk_arrive(p.ready + (size_t)grp * p.np_total, gpi, p.np_total, p.epoch, &poisoned,
                      reinterpret_cast<int*>(stat)))
     return;
   const int nc = min(64, p.G - cg * 64);
-  splitk_merge<8>(p.part_o, p.part_lse, p.out, p.H, p.rcap, p.np, nc, [&](int) { return r; },
+  splitk_merge<8>(p.part_o, p.part_lse, p.out, p.H, p.rcap, p.np_total, nc, [&](int) { return r; },
                   [&](int c) { return hl * p.G + cg * 64 + c; }, tid, poisoned);
 }
 

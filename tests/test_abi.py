@@ -271,8 +271,11 @@ def test_latent_validation():
     assert latent(s, c, scale=float("nan")) == PARAM
     assert latent(leaf(dtype=7), c) == DTYPE
     f8 = leaf(dtype=B.MSA_DTYPE_FP8_E4M3)
-    assert latent(s, f8) == DTYPE                              # leaves of two types
-    assert latent(f8, c) == DTYPE
+    # leaves of two types: accepted, and they need the split-K workspace even
+    # when one partition is asked for
+    assert latent(s, f8, ws=0) == NULL
+    assert latent(f8, c, ws=0, np_=1) == NULL
+    assert B.msa_latent_workspace_bytes(2, 1, 64, 1, 128, 512, 1) > 0
     # both FP8, or one FP8 leaf with the other not read: passes the type check
     assert latent(f8, leaf(dtype=B.MSA_DTYPE_FP8_E4M3), ws=0) == NULL
     assert latent(f8, None, top_c=0, lists=None, np_=1, ws=0) not in (NULL, SHAPE, PARAM, DTYPE)
@@ -292,7 +295,10 @@ def test_latent_partition_planning():
     assert B.msa_latent_partitions(4, 1, 64, 1, 128, 9872, 5) == 5
     assert B.msa_latent_partitions(4, 1, 64, 1, 128, 9872, 0) >= 5
     assert B.msa_latent_partitions(64, 1, 64, 1, 128, 1920, 1) == 1    # 32 tiles fit one
-    assert B.msa_latent_workspace_bytes(64, 1, 64, 1, 128, 1920, 1) == 0
+    # one partition and one leaf: no workspace; both leaves: the query
+    # reserves the two partitions that leaves of two types would take
+    assert B.msa_latent_workspace_bytes(64, 1, 64, 1, 0, 1920, 1) == 0
+    assert B.msa_latent_workspace_bytes(64, 1, 64, 1, 128, 1920, 1) > 0
     assert B.library().msa_latent_partitions(64, 1, 64, 1, 128, 1921, 1) == PARAM
     with pytest.raises(B.MsaError):
         B.msa_latent_partitions(4, 1, 64, 3, 128, 16, 0)

@@ -41,7 +41,9 @@ def check(wl, num_partitions=0, seqs=None, rows_per_seq=None):
     ref = L.latent_attention(pb, local)
     got = out[torch.tensor(rows, device=DEV, dtype=torch.long)]
     assert torch.isfinite(got.float()).all(), "non-finite output"
-    err = parity.check_attention(got, ref, wl.comp_dtype if wl.top_c else wl.swa_dtype, wl.name)
+    # the FP8 bar when a leaf the call reads is FP8
+    read = ([wl.swa_dtype] if wl.window else []) + ([wl.comp_dtype] if wl.top_c else [])
+    err = parity.check_attention(got, ref, "fp8_e4m3" if "fp8_e4m3" in read else "bf16", wl.name)
     say(f"  rows={len(rows)} max|err|={err:.3e}")
     return inp, out
 
@@ -169,6 +171,26 @@ def test_fp8_prefill_rows():
 
 def test_fp8_latent_decode_workload_sampled():
     check(LI.latent_decode_fp8(), seqs=[0, 21, 42, 63])
+
+
+MIXED = (dict(swa_dtype="bf16", comp_dtype="fp8_e4m3"), dict(swa_dtype="fp8_e4m3", comp_dtype="bf16"))
+
+
+@pytest.mark.parametrize("types", [0, 1])
+@pytest.mark.parametrize("np_", [0, 1, 2, 5])
+def test_leaves_of_two_storage_types(types, np_):
+    # the window leaf in one type and the compressed leaf in the other: one
+    # launch per leaf, the second merging both launches' partials; a row in
+    # its first window positions, invalid and repeated list values, a sink
+    check(wl(f"lat_mixed{types}_np{np_}", [1, 3, 2, 1], [700, 90, 1500, 0], [900, 150, 2000, 40],
+             H=64, window=96, top_c=300, sink_mean=1.0, sink_neg_inf_frac=0.25, bad_frac=0.05,
+             dup_frac=0.05, seed=40 + types, **MIXED[types]), num_partitions=np_)
+
+
+def test_leaves_of_two_storage_types_at_the_decode_workload_shape():
+    from dataclasses import replace
+    check(replace(LI.latent_decode(), name="latent_decode_mixed", swa_dtype="fp8_e4m3"),
+          seqs=[0, 17, 63])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
