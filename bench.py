@@ -258,11 +258,12 @@ def kernel_of(workload):
 
 
 def call_extra_kernels(workload):
-    """The other kernels one attention call launches (the latent call's
-    split-K combine; the plan and schedule kernels of the union-tile route)."""
+    """The other kernels one attention call launches: the plan and schedule
+    kernels of the union-tile route (split-K partials are merged inside the
+    attention kernels, so no combine launch)."""
     if is_reuse(workload):
         return ("prefill_plan_kernel", "attn_schedule_kernel")
-    return ("combine_kernel",) if is_latent(workload) else ()
+    return ()
 
 
 def reuse_sources(inp):
@@ -276,12 +277,12 @@ def reuse_sources(inp):
 def kernel_source_hash(workload="decode_batch64"):
     h = hashlib.sha256()
     if is_latent(workload):
-        files = ("msa_latent.hip", "msa_latent.h", "msa_lds.h", "msa_attention.hip", "msa_common.h",
+        files = ("msa_latent.hip", "msa_latent.h", "msa_lds.h", "msa_splitk.h", "msa_common.h",
                  "msa_kernels.h")
     elif is_reuse(workload):
         files = ("msa_prefill.hip", "msa_lds.h", "msa_common.h", "msa_kernels.h")
     else:
-        files = ("msa_attention.hip", "msa_common.h", "msa_kernels.h")
+        files = ("msa_attention.hip", "msa_splitk.h", "msa_common.h", "msa_kernels.h")
     for f in files:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
@@ -682,7 +683,7 @@ def run_latent(workload, args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(workload),
                      "kernel": "latent call: latent_attn_kernel" +
-                               (" + combine_kernel (split-K)" if np_ > 1 else "")},
+                               (" (split-K, partials merged in-kernel)" if np_ > 1 else "")},
         "cold_cache_ms": cold,
     }
     if not args.no_cpu_baseline:

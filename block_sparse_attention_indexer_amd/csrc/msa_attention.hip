@@ -105,6 +105,25 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     nU += __shfl(incl, 63);
   }
   __syncthreads();
+  // With several tokens per wave, the waves of one (sequence, KV head) all
+  // read the blocks every token selects (the first block and the newest
+  // ones).  The union is walked block 0 first, then newest first, so that
+  // the waves meet on those blocks at the same moment and fetch them from
+  // HBM once (the order of blocks does not change the softmax).
+  if (p.tpw > 1 && nU > 1) {
+    const int lo = uid[0] == 0 ? 1 : 0;
+    const int len = nU - lo;
+    for (int i = lane; i < len / 2; i += 64) {
+      const int a = lo + i, z = lo + len - 1 - i;
+      const int32_t ia = uid[a], iz = uid[z];
+      const uint32_t ma = umk[a], mz = umk[z];
+      uid[a] = iz;
+      uid[z] = ia;
+      umk[a] = mz;
+      umk[z] = ma;
+    }
+  }
+  __syncthreads();
 
   // ---- this partition's slice of the union --------------------------------
   const int per = (nU + p.np - 1) / p.np;
