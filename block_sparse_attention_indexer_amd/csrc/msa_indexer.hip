@@ -315,9 +315,10 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
   const int h0 = (idx % hgroups) * HPW;
   const int r0 = p.rg.offs[b];
   const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
+  const int clen = p.rg.clen[b];   // requested with the offsets: one round trip
   if (t >= n) return;
   const int nh = min(HPW, p.H_kv - h0);
-  const int pos = p.rg.clen[b] + t;
+  const int pos = clen + t;
   const int nb = min(pos / kBlock + 1, p.nbmax);
   const int r = r0 + t;
   int32_t* out0 = p.d_indices + ((size_t)r * p.H_kv + h0) * p.top_k;
@@ -365,10 +366,24 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
     // branch-free compare / ballot / popcount stream per bit).  Once
     // exactly kfree keys are at or above the threshold, no lower bit can
     // change which keys those are (equal keys at the boundary never give an
-    // exact count), so the search stops there: for distinct scores that is
-    // about half of the 32 steps.
-    uint32_t thr = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
+    // exact count), so the search stops there.
+    //
+    // The search starts below the leading bits that every candidate key
+    // shares (sign and exponent of scores of one magnitude, typically nine
+    // or more bits): at such a bit the search would take the shared value
+    // anyway (a 1 keeps all ncand > kfree keys, a 0 would keep none).  The
+    // highest bit where some candidate differs from the first one is found
+    // with six ballots over each lane's OR of differences.
+    const uint32_t ref = uniform(key[0]);   // lane 0, slot 0: always a candidate
+    uint32_t diff = 0u;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) diff |= s * 64 + lane < ncand ? key[s] ^ ref : 0u;
+    int top = -1;                           // highest differing bit, -1: all keys equal
+#pragma unroll
+    for (int step = 32; step >= 1; step >>= 1)
+      if (top + step <= 31 && ballot((diff >> (top + step)) != 0u)) top += step;
+    uint32_t thr = top < 0 ? ref : top == 31 ? 0u : ref & ~((2u << top) - 1u);
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
       int cnt = 0;
 #pragma unroll
