@@ -248,20 +248,24 @@ def is_reuse(workload):
     return workload.endswith("_reuse")
 
 
+def is_prefill(workload):
+    return workload.startswith("prefill")
+
+
 def kernel_of(workload):
-    """The dominant kernel of one attention call.  A reuse step calls
-    msa_attention_paged_shared, whose speculative rows run the union-tile
-    kernel."""
+    """The dominant kernel of one attention call: the union-tile kernel on
+    the prefill route and for a reuse step (whose msa_attention_paged_shared
+    runs its speculative rows through it), else the decode kernel."""
     if is_latent(workload):
         return "latent_attn_kernel"
-    return "attn_prefill3_kernel" if is_reuse(workload) else "attn_decode_kernel"
+    return "attn_prefill3_kernel" if is_reuse(workload) or is_prefill(workload) else "attn_decode_kernel"
 
 
 def call_extra_kernels(workload):
     """The other kernels one attention call launches: the plan and schedule
     kernels of the union-tile route (split-K partials are merged inside the
     attention kernels, so no combine launch)."""
-    if is_reuse(workload):
+    if is_reuse(workload) or is_prefill(workload):
         return ("prefill_plan_kernel", "attn_schedule_kernel")
     return ()
 
@@ -279,7 +283,7 @@ def kernel_source_hash(workload="decode_batch64"):
     if is_latent(workload):
         files = ("msa_latent.hip", "msa_latent.h", "msa_lds.h", "msa_splitk.h", "msa_common.h",
                  "msa_kernels.h")
-    elif is_reuse(workload):
+    elif is_reuse(workload) or is_prefill(workload):
         files = ("msa_prefill.hip", "msa_lds.h", "msa_common.h", "msa_kernels.h")
     else:
         files = ("msa_attention.hip", "msa_splitk.h", "msa_common.h", "msa_kernels.h")
@@ -428,6 +432,14 @@ def write_traffic_record(args):
                  "the unused rows of partly filled blocks and blocks that several token groups "
                  "of one sequence load separately."),
     }
+    if is_prefill(args.workload):
+        # q in and the output out: rows x query heads x 128 dims of BF16 each
+        qo = 2 * wl.total_rows * wl.num_q_heads * 128 * 2
+        rec["algorithmic_q_and_output_bytes_per_launch"] = int(qo)
+        rec["hbm_over_algorithmic_with_q_and_output"] = hbm / (algo + qo)
+        rec["note"] += (" On the prefill route q and the output (rows x query heads x 256 B "
+                        "each) dominate the call's own HBM bytes; the union blocks every tile "
+                        "stages into LDS come from L2 and the last-level cache, not HBM.")
     text = json.dumps(rec, indent=2) + "\n"
     if args.traffic_out:
         open(args.traffic_out, "w").write(text)
@@ -541,16 +553,15 @@ def run(workload, args):
     ms = wall / K * 1e3
     tok_s = wl.total_rows / (wall / K)
     # The roofline's duration is one attention call: the attention kernel
-    # alone on the decode routes with one partition; with split-K it also
-    # holds the combine launch (subtracting a separately timed combine would
-    # make the figure depend on launch gaps); on the prefill route it also
-    # holds the plan and schedule launches.
+    # alone on the decode routes (split-K partials are merged inside it); on
+    # the prefill route it also holds the plan and schedule launches.
     if prefill:
         metric_value = work["attn_flops"] / (wall / K) / 1e12
         unit = "TFLOP/s"
         achieved = work["attn_flops"] / (att_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                "traffic": traffic_record(workload),
                 "kernel": "prefill attention call: prefill_plan_kernel + attn_schedule_kernel + "
                           "attn_prefill3_kernel"}
     else:
