@@ -105,22 +105,67 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     nU += __shfl(incl, 63);
   }
   __syncthreads();
-  // With several tokens per wave, the waves of one (sequence, KV head) all
-  // read the blocks every token selects (the first block and the newest
-  // ones).  The union is walked block 0 first, then newest first, so that
-  // the waves meet on those blocks at the same moment and fetch them from
-  // HBM once (the order of blocks does not change the softmax).
+  // With several tokens per wave (speculative rows), the waves of one
+  // (sequence, KV head) need many of the same blocks: every token's first
+  // and newest blocks, and the picks their tokens share.  Such a block costs
+  // one HBM fetch only if the waves reach it at about the same moment (an
+  // L2 line does not outlive a block's worth of another wave's streaming),
+  // so each wave walks its union ordered by how many of the workgroup's
+  // waves need the block, most first, then by id: the blocks every wave
+  // needs come first in the same order everywhere, then those most waves
+  // need.  (The order of blocks does not change the softmax.)  Unions of
+  // more than 256 blocks are walked block 0 first, then newest first.
   if (p.tpw > 1 && nU > 1) {
-    const int lo = uid[0] == 0 ? 1 : 0;
-    const int len = nU - lo;
-    for (int i = lane; i < len / 2; i += 64) {
-      const int a = lo + i, z = lo + len - 1 - i;
-      const int32_t ia = uid[a], iz = uid[z];
-      const uint32_t ma = umk[a], mz = umk[z];
-      uid[a] = iz;
-      uid[z] = ia;
-      umk[a] = mz;
-      umk[z] = ma;
+    if (W > 1 && nU <= 256) {
+      int32_t eid[4];
+      uint32_t emk[4];
+      int ecls[4], epos[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = lane + 64 * q;
+        ecls[q] = 0;
+        if (i < nU) {
+          eid[q] = uid[i];
+          emk[q] = umk[i];
+          int nw = 1;
+          for (int w2 = 0; w2 < W; ++w2) {
+            if (w2 == wave) continue;
+            const uint32_t* bm2 = lds + w2 * (p.tpw * nbw + 2 * cap);
+            uint32_t any = 0u;
+            for (int tl = 0; tl < p.tpw; ++tl) any |= bm2[tl * nbw + (eid[q] >> 5)];
+            nw += (any >> (eid[q] & 31)) & 1u;
+          }
+          ecls[q] = nw;
+        }
+      }
+      int pos = 0;
+      for (int cl = W; cl >= 1; --cl) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint64_t m = ballot(ecls[q] == cl);
+          if (ecls[q] == cl) epos[q] = pos + mask_rank(m);
+          pos += __popcll(m);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (ecls[q] > 0) {
+          uid[epos[q]] = eid[q];
+          umk[epos[q]] = emk[q];
+        }
+      }
+    } else {
+      const int lo = uid[0] == 0 ? 1 : 0;
+      const int len = nU - lo;
+      for (int i = lane; i < len / 2; i += 64) {
+        const int a = lo + i, z = lo + len - 1 - i;
+        const int32_t ia = uid[a], iz = uid[z];
+        const uint32_t ma = umk[a], mz = umk[z];
+        uid[a] = iz;
+        uid[z] = ia;
+        umk[a] = mz;
+        umk[z] = ma;
+      }
     }
   }
   __syncthreads();
