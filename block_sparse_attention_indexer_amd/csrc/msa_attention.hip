@@ -109,50 +109,94 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   // (sequence, KV head) need many of the same blocks: every token's first
   // and newest blocks, and the picks their tokens share.  Such a block costs
   // one HBM fetch only if the waves reach it at about the same moment (an
-  // L2 line does not outlive a block's worth of another wave's streaming),
-  // so each wave walks its union ordered by how many of the workgroup's
-  // waves need the block, most first, then by id: the blocks every wave
-  // needs come first in the same order everywhere, then those most waves
-  // need.  (The order of blocks does not change the softmax.)  Unions of
-  // more than 256 blocks are walked block 0 first, then newest first.
+  // L2 line does not outlive much of another wave's streaming), so the
+  // waves walk their unions on one common schedule.  The blocks that more
+  // than one wave needs form one global order (most waves first, then by
+  // id); step g of every wave is global block g if the wave needs it, else
+  // the wave's next block that no other wave needs, while those last.  So
+  // wave w's k-th shared block, at global index g, sits at k + min(P, g -
+  // k) (P: its private blocks), and its private block j at j + #{shared k :
+  // g - k <= j}.  Counting waves per block is bit-sliced over the
+  // workgroup's block bitmaps, one 32-block word per lane.  Unions of more
+  // than 64 blocks, or bitmaps of more than 64 words, are walked block 0
+  // first, then newest first.  (The order of blocks does not change the
+  // softmax.)
   if (p.tpw > 1 && nU > 1) {
-    if (W > 1 && nU <= 256) {
-      int32_t eid[4];
-      uint32_t emk[4];
-      int ecls[4], epos[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = lane + 64 * q;
-        ecls[q] = 0;
-        if (i < nU) {
-          eid[q] = uid[i];
-          emk[q] = umk[i];
-          int nw = 1;
-          for (int w2 = 0; w2 < W; ++w2) {
-            if (w2 == wave) continue;
-            const uint32_t* bm2 = lds + w2 * (p.tpw * nbw + 2 * cap);
-            uint32_t any = 0u;
-            for (int tl = 0; tl < p.tpw; ++tl) any |= bm2[tl * nbw + (eid[q] >> 5)];
-            nw += (any >> (eid[q] & 31)) & 1u;
-          }
-          ecls[q] = nw;
+    if (W > 1 && nU <= 64 && nbw <= 64) {
+      // -- blocks needed by exactly 2, 3 and 4 waves, per 32-block word --
+      uint32_t E2 = 0u, E3 = 0u, E4 = 0u;
+      if (lane < nbw) {
+        uint32_t u[4] = {0u, 0u, 0u, 0u};   // W <= 4 waves per workgroup
+        for (int w2 = 0; w2 < W; ++w2) {
+          const uint32_t* bm2 = lds + w2 * (p.tpw * nbw + 2 * cap);
+          uint32_t any = 0u;
+          for (int tl = 0; tl < p.tpw; ++tl) any |= bm2[tl * nbw + lane];
+          u[w2] = any;
         }
+        // per-bit count of four words: bits b0 + 2 b1 + 4 b2
+        const uint32_t s01 = u[0] ^ u[1], c01 = u[0] & u[1], s23 = u[2] ^ u[3], c23 = u[2] & u[3];
+        const uint32_t b0 = s01 ^ s23, k1 = s01 & s23;
+        const uint32_t b1 = c01 ^ c23 ^ k1, b2 = (c01 & c23) | ((c01 ^ c23) & k1);
+        E2 = ~b0 & b1 & ~b2;
+        E3 = b0 & b1;
+        E4 = b2;
       }
-      int pos = 0;
-      for (int cl = W; cl >= 1; --cl) {
+      // exclusive prefix counts over words (one 64-bit scan of three
+      // 21-bit fields) and totals
+      const uint64_t own = (uint64_t)__popc(E2) | ((uint64_t)__popc(E3) << 21) | ((uint64_t)__popc(E4) << 42);
+      uint64_t incl = own;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint64_t m = ballot(ecls[q] == cl);
-          if (ecls[q] == cl) epos[q] = pos + mask_rank(m);
-          pos += __popcll(m);
-        }
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t lo = __shfl_up((uint32_t)incl, off), hi = __shfl_up((uint32_t)(incl >> 32), off);
+        if (lane >= off) incl += ((uint64_t)hi << 32) | lo;
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (ecls[q] > 0) {
-          uid[epos[q]] = eid[q];
-          umk[epos[q]] = emk[q];
-        }
+      const uint64_t excl = incl - own;
+      const uint64_t tot = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(incl >> 32), 63) << 32) |
+                           __builtin_amdgcn_readlane((uint32_t)incl, 63);
+      auto field = [](uint64_t v, int c) { return (int)((v >> (21 * (c - 2))) & 0x1FFFFFu); };
+      // -- this wave's entries, one per lane --------------------------------
+      const bool has = lane < nU;
+      const int x = has ? uid[lane] : 0;
+      const uint32_t mk = has ? umk[lane] : 0u;
+      const int wd = x >> 5;
+      const uint32_t e2 = __shfl(E2, wd), e3 = __shfl(E3, wd), e4 = __shfl(E4, wd);
+      const uint32_t pw_lo = __shfl((uint32_t)excl, wd), pw_hi = __shfl((uint32_t)(excl >> 32), wd);
+      const uint64_t pw = ((uint64_t)pw_hi << 32) | pw_lo;
+      const uint32_t bit = 1u << (x & 31);
+      const int cls = !has ? 0 : (e4 & bit) ? 4 : (e3 & bit) ? 3 : (e2 & bit) ? 2 : 1;
+      const uint32_t ec = cls == 4 ? e4 : cls == 3 ? e3 : e2;
+      int gidx = 0;   // global index of a shared block
+      if (cls >= 2) {
+        for (int c2 = cls + 1; c2 <= 4; ++c2) gidx += field(tot, c2);
+        gidx += field(pw, cls) + __popc(ec & (bit - 1u));
+      }
+      // rank among this wave's shared blocks in the global order (classes
+      // high to low, ids ascending within a class), and among its private ones
+      int rnk = 0, nshared = 0;
+      for (int cl = 4; cl >= 2; --cl) {
+        const uint64_t m = ballot(cls == cl);
+        if (cls == cl) rnk = nshared + mask_rank(m);
+        nshared += __popcll(m);
+      }
+      {
+        const uint64_t m = ballot(cls == 1);
+        if (cls == 1) rnk = mask_rank(m);
+      }
+      const int npriv = nU - nshared;
+      const int dgap = gidx - rnk;   // shared: global steps before it not taken by its own shared blocks
+      // shared blocks placed before private block rnk (the ballot and the
+      // walk over shared lanes run with every lane active)
+      int before = 0;
+      uint64_t sm = ballot(cls >= 2);
+      while (sm) {
+        const int t = __builtin_ctzll(sm);
+        sm &= sm - 1;
+        before += __builtin_amdgcn_readlane(dgap, t) <= rnk;
+      }
+      const int npos = cls >= 2 ? rnk + min(npriv, dgap) : rnk + before;
+      if (has) {
+        uid[npos] = x;
+        umk[npos] = mk;
       }
     } else {
       const int lo = uid[0] == 0 ? 1 : 0;
