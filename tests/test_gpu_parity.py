@@ -180,6 +180,31 @@ def test_top_k_over_a_few_thousand_candidates():
                             top_k=100, init=2, local=3))
 
 
+@pytest.mark.parametrize("case", ["union64", "bitmap65", "mixed_paths"])
+def test_speculative_block_schedule_edges(case):
+    # The waves of a speculative (sequence, KV head) walk their unions on one
+    # common schedule when a wave's union has at most 64 blocks and the block
+    # bitmaps at most 64 words, else block 0 first and then newest first.
+    # union64: no forced blocks and 32 picks from ~1500 candidates, so two
+    #   tokens' unions are mostly exactly 64 blocks; 3 to 4 waves per
+    #   workgroup (5 to 8 draft tokens, two per wave).
+    # bitmap65: one context of 2049 blocks makes the bitmaps 65 words: every
+    #   wave takes the fallback order.
+    # mixed_paths: 40 picks per token, so some waves of a workgroup hold
+    #   more than 64 blocks and take the fallback while the others follow
+    #   the schedule.
+    if case == "union64":
+        wl = wl_custom("sched_union64", [5, 6, 8, 3], [190000, 150000, 120000, 170000], H_kv=1,
+                       top_k=32, init=0, local=0, seed=21)
+    elif case == "bitmap65":
+        wl = wl_custom("sched_bitmap65", [4, 2], [2049 * 128 + 5, 3000], H_kv=1, top_k=32,
+                       init=1, local=2, seed=22)
+    else:
+        wl = wl_custom("sched_mixed", [7, 4, 2], [100000, 50000, 9000], H_kv=2, top_k=40,
+                       init=1, local=1, seed=23)
+    run_and_check(wl, chunk=1)
+
+
 def test_two_column_groups_per_sequence():
     # 16 KV heads sharing one index head x 8 draft tokens = 128 columns
     run_and_check(wl_custom("cg2", [8, 3, 6], [3000, 5000, 700], H_kv=16, G=1, top_k=5))
