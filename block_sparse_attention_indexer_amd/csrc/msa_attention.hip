@@ -119,14 +119,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   // g - k <= j}.  Counting waves per block is bit-sliced over the
   // workgroup's block bitmaps, one 32-block word per lane.  Unions of more
   // than 64 blocks, or bitmaps of more than 64 words, are walked block 0
-  // first, then newest first.  (The order of blocks does not change the
-  // softmax.)
+  // first, then newest first, as are workgroups of more than four waves
+  // (the bit-sliced count takes four).  The order of blocks changes only
+  // the rounding order of the softmax sums.
   if (p.tpw > 1 && nU > 1) {
-    if (W > 1 && nU <= 64 && nbw <= 64) {
+    if (W > 1 && W <= 4 && nU <= 64 && nbw <= 64) {
       // -- blocks needed by exactly 2, 3 and 4 waves, per 32-block word --
       uint32_t E2 = 0u, E3 = 0u, E4 = 0u;
       if (lane < nbw) {
-        uint32_t u[4] = {0u, 0u, 0u, 0u};   // W <= 4 waves per workgroup
+        uint32_t u[4] = {0u, 0u, 0u, 0u};
         for (int w2 = 0; w2 < W; ++w2) {
           const uint32_t* bm2 = lds + w2 * (p.tpw * nbw + 2 * cap);
           uint32_t any = 0u;
