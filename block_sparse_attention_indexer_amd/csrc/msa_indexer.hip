@@ -296,16 +296,32 @@ hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_
 // score loads' latency worth sharing between heads.
 //
 // Candidates are the blocks [init, nb - local) (everything not forced).  The
-// (top_k - |forced|)-th largest score is found by building its
-// order-preserving 32-bit key one bit at a time from the top (each step
-// counts keys >= the trial value with a wave ballot).  Blocks strictly above
-// the threshold are taken, then the lowest-id blocks equal to it until the
-// count is reached.  Output is emitted in ascending id order by ballot
-// prefix counts, so no sort is needed: forced-first, chosen candidates,
-// forced-newest are already ascending ranges.
+// (top_k - |forced|)-th largest score is found as its order-preserving
+// 32-bit key by a radix select, eight bits per round from the highest bit
+// where candidate keys differ: a round counts the keys that match the bits
+// decided so far into 256 LDS bins by their next eight bits and takes the
+// highest bin at which the count from the top reaches what is still needed
+// (bins summed in 16 groups of 16, each level a 16-lane suffix scan).
+// Blocks strictly above the threshold are taken, then the lowest-id blocks
+// equal to it until the count is reached.  Output is emitted in ascending id
+// order by ballot prefix counts, so no sort is needed: forced-first, chosen
+// candidates, forced-newest are already ascending ranges.
 // ---------------------------------------------------------------------------
+
+// Sum of lanes j .. 15 of this lane's 16-lane row (lanes past the row add 0).
+__device__ __forceinline__ int row_suffix_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x101, 0xf, 0xf, true);   // row_shl:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x102, 0xf, 0xf, true);   // row_shl:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x104, 0xf, 0xf, true);   // row_shl:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x108, 0xf, 0xf, true);   // row_shl:8
+  return x;
+}
+
 template <int KPL, int HPW>
 __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
+  // per wave: 256 radix bins, then one bin per lane that takes the adds of
+  // keys outside the round (never read), so the adds need no branch
+  __shared__ u32x4 hist_lds[4][80];
   const int lane = threadIdx.x & 63;
   const int wave = uniform((int)(threadIdx.x >> 6));
   const int b = blockIdx.y;
@@ -340,19 +356,16 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
 
   const float* sc0 = p.scores + ((size_t)r * p.H_kv + h0) * p.score_stride + p.init;
   const int nslot = (ncand + 63) / 64;
-  // Every head's candidate slots are requested before any is used (lanes
+  // Every head's candidate slots are requested before any is used (slots
   // past the end read the last candidate), so one memory latency covers
   // the wave's heads; keys past the candidates are 0, below every real key.
   float v[HPW][KPL];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int s = 0; s < KPL; ++s) v[hh][s] = 0.f;
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
     for (int s = 0; s < KPL; ++s)
-      if (hh < nh && s < nslot) v[hh][s] = sc0[(size_t)hh * p.score_stride + min(s * 64 + lane, ncand - 1)];
+      v[hh][s] = HPW == 1 || hh < nh ? sc0[(size_t)hh * p.score_stride + min(s * 64 + lane, ncand - 1)] : 0.f;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(hist_lds[wave]);
 
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
@@ -360,20 +373,16 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
     int32_t* out = out0 + (size_t)hh * p.top_k;
     uint32_t key[KPL];
 #pragma unroll
-    for (int s = 0; s < KPL; ++s) key[s] = s * 64 + lane < ncand ? score_key(v[hh][s]) : 0u;
-    // Keys of slots past the candidates are 0, below every candidate key
-    // and below every trial value, so the counts need no per-slot guard (a
-    // branch-free compare / ballot / popcount stream per bit).  Once
-    // exactly kfree keys are at or above the threshold, no lower bit can
-    // change which keys those are (equal keys at the boundary never give an
-    // exact count), so the search stops there.
-    //
+    for (int s = 0; s < KPL; ++s) {
+      const uint32_t k = score_key(v[hh][s]);
+      key[s] = s * 64 + lane < ncand ? k : 0u;
+    }
     // The search starts below the leading bits that every candidate key
-    // shares (sign and exponent of scores of one magnitude, typically nine
-    // or more bits): at such a bit the search would take the shared value
-    // anyway (a 1 keeps all ncand > kfree keys, a 0 would keep none).  The
-    // highest bit where some candidate differs from the first one is found
-    // with six ballots over each lane's OR of differences.
+    // shares (sign and exponent of scores of one magnitude, typically six
+    // or more bits): the threshold takes the shared value there (a 1 keeps
+    // all ncand > kfree keys, a 0 would keep none).  The highest bit where
+    // some candidate differs from the first one is found with six ballots
+    // over each lane's OR of differences.
     const uint32_t ref = uniform(key[0]);   // lane 0, slot 0: always a candidate
     uint32_t diff = 0u;
 #pragma unroll
@@ -383,21 +392,75 @@ __global__ __launch_bounds__(256) void topk_kernel(IndexerParams p) {
     for (int step = 32; step >= 1; step >>= 1)
       if (top + step <= 31 && ballot((diff >> (top + step)) != 0u)) top += step;
     uint32_t thr = top < 0 ? ref : top == 31 ? 0u : ref & ~((2u << top) - 1u);
-    for (int bit = top; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int cnt = 0;
+    // Radix rounds over bits hb .. hb - w + 1.  Invariant: `gt_keys` keys
+    // exceed thr in the bits decided so far, fewer than kfree, and at least
+    // kfree - gt_keys of the keys matching thr there remain, so some bin
+    // reaches the need and the round's choice exists.  Once exactly kfree
+    // keys are at or above the threshold, no lower bit can change which keys
+    // those are (equal keys at the boundary never give an exact count), so
+    // the search stops there.
+    int gt_keys = 0;
+    bool exact = false;
+    for (int hb = top; hb >= 0;) {
+      const int w = min(8, hb + 1), sh = hb + 1 - w;
+      const uint32_t hi = hb == 31 ? 0u : ~((2u << hb) - 1u);   // bits already decided
+      const uint32_t pre = thr & hi;
+      hist_lds[wave][lane] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int s = 0; s < KPL; ++s) cnt += __popcll(ballot(key[s] >= cand));
-      if (cnt >= kfree) {
-        thr = cand;
-        if (cnt == kfree) break;
+      for (int s = 0; s < KPL; ++s) {
+        const bool in = (s * 64 + lane < ncand) & ((key[s] & hi) == pre);
+        const uint32_t bin = in ? (key[s] >> sh) & ((1u << w) - 1u) : 256u + lane;
+        __hip_atomic_fetch_add(hist + bin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
       }
+      const int need = kfree - gt_keys;
+      // group j = bins 16 j .. 16 j + 15, suffix counts over groups
+      int gs = 0;
+      if (lane < 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 c4 = hist_lds[wave][4 * lane + q];
+          gs += (int)(c4[0] + c4[1] + c4[2] + c4[3]);
+        }
+      }
+      gs = row_suffix_sum(gs);
+      // (bit 0 only guards the count of leading zeros: the invariant puts
+      // group 0 and bin 0 of a group at or above the need)
+      const int G = 63 - __builtin_clzll(ballot(lane < 16 && gs >= need) | 1ull);
+      const int g_above = G == 15 ? 0 : __builtin_amdgcn_readlane(gs, G + 1);
+      int bs = lane < 16 ? (int)hist[16 * G + lane] : 0;
+      bs = row_suffix_sum(bs);
+      const int j = 63 - __builtin_clzll(ballot(lane < 16 && g_above + bs >= need) | 1ull);
+      const int n_ge = g_above + __builtin_amdgcn_readlane(bs, j);              // bins >= 16 G + j
+      const int n_gt = g_above + (j == 15 ? 0 : __builtin_amdgcn_readlane(bs, j + 1));
+      thr |= (uint32_t)(16 * G + j) << sh;
+      if (n_ge == need) {
+        exact = true;
+        break;
+      }
+      gt_keys += n_gt;
+      hb -= w;
     }
+    int run = 0;
+    if (exact) {
+      // the candidates at or above the threshold are exactly the kfree chosen
+#pragma unroll
+      for (int s = 0; s < KPL; ++s) {
+        if (s < nslot) {
+          const bool sel = s * 64 + lane < ncand && key[s] >= thr;
+          const uint64_t sm = ballot(sel);
+          if (sel) out[p.init + run + mask_rank(sm)] = p.init + s * 64 + lane;
+          run += __popcll(sm);
+        }
+      }
+      continue;
+    }
+    // equal keys straddle the cut: all above it, then the lowest ids equal
+    // to it (keys past the candidates rank after every candidate)
     int above = 0;
 #pragma unroll
     for (int s = 0; s < KPL; ++s) above += __popcll(ballot(key[s] > thr));
     const int need_eq = kfree - above;
-    int run = 0, run_eq = 0;
+    int run_eq = 0;
 #pragma unroll
     for (int s = 0; s < KPL; ++s) {
       if (s < nslot) {

@@ -221,6 +221,33 @@ def test_tie_break_lower_id_on_all_equal_scores():
     assert list(d[2, 0]) == [0, 1, 2, 3, 8, 9]
 
 
+@pytest.mark.parametrize("name,new,cached,top_k", [
+    ("decode_kpl4", [1, 1], [3000, 200 * 128 + 5], 40),
+    ("decode_kpl16", [1], [900 * 128], 40),
+    ("decode_kpl64", [1], [3000 * 128 + 17], 64),
+    ("decode_kpl128", [1], [5000 * 128], 100),
+    ("spec", [3, 5], [900 * 128, 150 * 128 + 9], 40),
+    ("prefill", [40, 12], [2000, 250 * 128], 30),
+])
+def test_tied_block_scores_select_lowest_ids(name, new, cached, top_k):
+    # Index keys constant over a block, c_b times a unit vector with c_b a
+    # small integer of either sign, so every block score is exactly c_b q[0]
+    # in any precision: large groups of equal scores, the cut falling inside
+    # one, and scores of both signs.  The selection is then unique (equal
+    # scores go to the lower block id) and must match the oracle exactly.
+    wl = wl_custom(f"tiedscores_{name}", new, cached, top_k=top_k, init=1, local=2, seed=31)
+    say(f"[case] {wl.name}")
+    inp = I.make_inputs(wl, DEV)
+    P = inp.index_k.shape[0]
+    c = torch.from_numpy(np.random.default_rng(5).integers(-20, 21, size=P)).to(DEV, torch.float32)
+    inp.index_k.zero_()
+    inp.index_k[:, :, :, 0] = c.view(P, 1, 1).to(torch.bfloat16)
+    d_gpu = B.run_indexer(inp).cpu().numpy()
+    pb, orig_rows = O.problem_for_sequences(inp, range(wl.batch))
+    d_ref, _ = O.indexer(pb)
+    assert np.array_equal(d_gpu[orig_rows], d_ref)
+
+
 def test_page_permutation_gives_bitwise_identical_results():
     wl = wl_custom("perm", [1, 3], [7000, 2000], top_k=8)
     inp = I.make_inputs(wl, DEV)
