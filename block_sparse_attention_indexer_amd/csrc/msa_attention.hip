@@ -28,6 +28,21 @@
 
 namespace msa {
 
+// Exclusive prefix over the wave's lanes of a per-lane count 0 <= v < 64,
+// and the wave's total: one ballot per bit of the count, so no cross-lane
+// shuffle chain.
+__device__ __forceinline__ void wave_prefix_small(int v, int* before, int* total) {
+  int bsum = 0, tsum = 0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const uint64_t bk = ballot((v >> k) & 1);
+    bsum += mask_rank(bk) << k;
+    tsum += __popcll(bk) << k;
+  }
+  *before = bsum;
+  *total = tsum;
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   extern __shared__ uint32_t lds[];
@@ -67,42 +82,89 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   uint32_t* bm = lds + wave * (p.tpw * nbw + 2 * cap);
   int32_t* uid = reinterpret_cast<int32_t*>(bm + p.tpw * nbw);
   uint32_t* umk = reinterpret_cast<uint32_t*>(uid + cap);
-  for (int i = lane; i < p.tpw * nbw; i += 64) bm[i] = 0u;
-  __syncthreads();
-  for (int tl = 0; tl < ntok; ++tl) {
-    const int tok = tok0 + tl;
-    const int nbt = min((c + tok) / kBlock + 1, p.nbmax);
-    const int32_t* lst = p.d_indices + ((size_t)(r0 + tok) * p.H_kv + h) * p.top_k;
-    for (int i = lane; i < p.top_k; i += 64) {
-      const int id = lst[i];
-      if (id >= 0 && id < nbt) atomicOr(&bm[tl * nbw + (id >> 5)], 1u << (id & 31));
-    }
-  }
-  __syncthreads();
   int nU = 0;
-  for (int w0 = 0; w0 < nbw; w0 += 64) {
-    const int w = w0 + lane;
-    uint32_t u = 0u;
-    if (w < nbw)
-      for (int tl = 0; tl < ntok; ++tl) u |= bm[tl * nbw + w];
-    const int cnt = __popc(u);
-    int incl = cnt;
+  // One token per wave (decode): when the row's valid ids come first and
+  // ascend, as the indexer writes them, the row is the union itself.  Each
+  // entry's page is then requested as soon as its id arrives and kept in
+  // umk (the token mask is 1), so the page lookup needs no round trip of its
+  // own after the union is built.  Other rows take the bitmap below.
+  bool ids_in_order = false;
+  if (p.tpw == 1 && W == 1 && ntok == 1) {
+    const int nbt = min((c + tok0) / kBlock + 1, p.nbmax);
+    const int32_t* lst = p.d_indices + ((size_t)(r0 + tok0) * p.H_kv + h) * p.top_k;
+    bool ok = true, seen_invalid = false;
+    for (int i0 = 0; i0 < p.top_k; i0 += 64) {
+      const int i = i0 + lane;
+      const int id = i < p.top_k ? lst[i] : -1;
+      const bool valid = id >= 0 && id < nbt;
+      const uint64_t vm = ballot(valid);
+      // valid entries must form a prefix of the row
+      ok = ok && (vm & (vm + 1ull)) == 0ull && !(seen_invalid && vm != 0ull);
+      seen_invalid = seen_invalid || vm != ~0ull;
+      if (i < p.top_k) {
+        uid[i] = id;
+        umk[i] = valid ? (uint32_t)p.rg.table[(size_t)b * p.rg.stride + id] : 0u;
+      }
+      nU += __popcll(vm);
+    }
+    __syncthreads();   // (one wave) the ids of every lane are in LDS
+    // strictly ascending: each valid entry above the one before it
+    for (int i0 = 0; i0 < nU; i0 += 64) {
+      const int i = i0 + lane;
+      if (ballot(i > 0 && i < nU && uid[i - 1] >= uid[i]) != 0ull) ok = false;
+    }
+    ids_in_order = ok;
+    if (!ok) nU = 0;
+  }
+  if (!ids_in_order) {
+    for (int i = lane; i < p.tpw * nbw; i += 64) bm[i] = 0u;
+    __syncthreads();
+    for (int tl = 0; tl < ntok; ++tl) {
+      const int tok = tok0 + tl;
+      const int nbt = min((c + tok) / kBlock + 1, p.nbmax);
+      const int32_t* lst = p.d_indices + ((size_t)(r0 + tok) * p.H_kv + h) * p.top_k;
+      for (int i = lane; i < p.top_k; i += 64) {
+        const int id = lst[i];
+        if (id >= 0 && id < nbt) atomicOr(&bm[tl * nbw + (id >> 5)], 1u << (id & 31));
+      }
+    }
+    __syncthreads();
+    // Each lane takes one 32-block word: its set bits in ascending order go
+    // to consecutive union slots after the lanes below it.  The tokens'
+    // words are kept in registers (T: a bound on the wave's tokens, at most
+    // 16), and the exclusive prefix of the per-lane counts (at most 32) is
+    // summed over six ballots, one per bit of the count.
+    auto build = [&](auto tmax) {
+      constexpr int T = decltype(tmax)::value;
+      for (int w0 = 0; w0 < nbw; w0 += 64) {
+        const int w = w0 + lane;
+        uint32_t wd[T];
+        uint32_t u = 0u;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    int pos = nU + incl - cnt;
-    while (u) {
-      const int bit = __ffs(u) - 1;
-      u &= u - 1u;
-      uint32_t mk = 0u;
-      for (int tl = 0; tl < ntok; ++tl) mk |= ((bm[tl * nbw + w] >> bit) & 1u) << tl;
-      uid[pos] = w * 32 + bit;
-      umk[pos] = mk;
-      ++pos;
-    }
-    nU += __shfl(incl, 63);
+        for (int tl = 0; tl < T; ++tl) {
+          wd[tl] = tl < ntok && w < nbw ? bm[tl * nbw + w] : 0u;
+          u |= wd[tl];
+        }
+        int before = 0, total = 0;
+        wave_prefix_small(__popc(u), &before, &total);
+        int pos = nU + before;
+        while (u) {
+          const int bit = __ffs(u) - 1;
+          u &= u - 1u;
+          uint32_t mk = 0u;
+#pragma unroll
+          for (int tl = 0; tl < T; ++tl) mk |= ((wd[tl] >> bit) & 1u) << tl;
+          uid[pos] = w * 32 + bit;
+          umk[pos] = mk;
+          ++pos;
+        }
+        nU += total;
+      }
+    };
+    if (p.tpw <= 2) build(std::integral_constant<int, 2>{});
+    else if (p.tpw <= 4) build(std::integral_constant<int, 4>{});
+    else if (p.tpw <= 8) build(std::integral_constant<int, 8>{});
+    else build(std::integral_constant<int, 16>{});
   }
   __syncthreads();
   // With several tokens per wave (speculative rows), the waves of one
@@ -142,18 +204,19 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
         E3 = b0 & b1;
         E4 = b2;
       }
-      // exclusive prefix counts over words (one 64-bit scan of three
-      // 21-bit fields) and totals
-      const uint64_t own = (uint64_t)__popc(E2) | ((uint64_t)__popc(E3) << 21) | ((uint64_t)__popc(E4) << 42);
-      uint64_t incl = own;
+      // exclusive prefix counts over words and totals, per class, packed
+      // as three 21-bit fields (class c at bit 21 (c - 2))
+      uint64_t excl = 0ull, tot = 0ull;
+      {
+        const uint32_t ew[3] = {E2, E3, E4};
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t lo = __shfl_up((uint32_t)incl, off), hi = __shfl_up((uint32_t)(incl >> 32), off);
-        if (lane >= off) incl += ((uint64_t)hi << 32) | lo;
+        for (int f = 0; f < 3; ++f) {
+          int bf = 0, tf = 0;
+          wave_prefix_small(__popc(ew[f]), &bf, &tf);
+          excl |= (uint64_t)bf << (21 * f);
+          tot |= (uint64_t)tf << (21 * f);
+        }
       }
-      const uint64_t excl = incl - own;
-      const uint64_t tot = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(incl >> 32), 63) << 32) |
-                           __builtin_amdgcn_readlane((uint32_t)incl, 63);
       auto field = [](uint64_t v, int c) { return (int)((v >> (21 * (c - 2))) & 0x1FFFFFu); };
       // -- this wave's entries, one per lane --------------------------------
       const bool has = lane < nU;
@@ -277,7 +340,13 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     if (lane < nS) {
       blk_lane = uid[e_lo + s0 + lane];
       mk_lane = umk[e_lo + s0 + lane];
-      const int pg = p.rg.table[(size_t)b * p.rg.stride + blk_lane];
+      int pg;
+      if (ids_in_order) {   // umk holds the page; the one token's mask is 1
+        pg = (int)mk_lane;
+        mk_lane = 1u;
+      } else {
+        pg = p.rg.table[(size_t)b * p.rg.stride + blk_lane];
+      }
       pg_lane = (unsigned)pg < (unsigned)p.k.num_pages ? pg : -1;   // bad ids: block skipped
       if (pg_lane < 0) report_error(p.err, kErrPage);
     }
