@@ -19,13 +19,11 @@ namespace msa {
 // to 16 * NCT columns, a column being one (token, KV head) pair of a sequence
 // whose KV head reads index-K head hk (one shared head, or one per KV head).
 // Units are ordered (sequence, hk, column group, block) and split into equal
-// contiguous shares, one per wave, so that every wave streams the same
-// number of bytes whatever the mix of context lengths.  The grid holds one
-// round of resident waves, or two with one column tile per unit, where the
-// second round's waves start as the first round's finish and so even out
-// the first round's uneven streaming speeds.  Each workgroup recomputes the
-// per-sequence unit counts from the ragged metadata (a prefix over chunks of
-// sequences in LDS) rather than reading a plan written by another launch.
+// contiguous shares, one per wave of a grid sized to be resident at once, so
+// that every wave streams the same number of bytes whatever the mix of
+// context lengths.  Each workgroup recomputes the per-sequence unit counts
+// from the ragged metadata (a prefix over chunks of sequences in LDS) rather
+// than reading a plan written by another launch.
 //
 // A wave walks its share in segments that stay inside one column group.  Per
 // segment it loads the page ids with one vector load and the query columns
@@ -270,17 +268,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
   }
 }
 
-// Waves the scorer keeps resident per CU (register-limited occupancy), and
-// the rounds of them its grid holds.
+// Waves the scorer keeps resident per CU (register-limited occupancy; the
+// equal shares assume every wave of the grid is resident at once).
 constexpr int score_waves_per_cu(int nct, bool fp8) { return nct >= 4 ? 4 : (fp8 && nct == 1) ? 12 : 8; }
-constexpr int score_rounds(int nct) { return nct == 1 ? 2 : 1; }
 
 hipError_t launch_indexer_decode(const IndexerParams& p, int num_cus, hipStream_t s) {
   const int hpi = p.H_kv / p.H_ik;
   const int cols = p.rg.max_seq * hpi;
   const int nct = cols <= 16 ? 1 : cols <= 32 ? 2 : 4;
   const int ncg = (cols + 16 * nct - 1) / (16 * nct);
-  dim3 grid(score_rounds(nct) * num_cus * score_waves_per_cu(nct, p.ik_fp8 != 0) / kIdxWaves);
+  dim3 grid(num_cus * score_waves_per_cu(nct, p.ik_fp8 != 0) / kIdxWaves);
   if (p.ik_fp8) {
     if (nct == 1) hipLaunchKernelGGL((indexer_score_kernel<1, true>), grid, dim3(kIdxThreads), 0, s, p, ncg);
     else if (nct == 2) hipLaunchKernelGGL((indexer_score_kernel<2, true>), grid, dim3(kIdxThreads), 0, s, p, ncg);
