@@ -248,6 +248,31 @@ def test_tied_block_scores_select_lowest_ids(name, new, cached, top_k):
     assert np.array_equal(d_gpu[orig_rows], d_ref)
 
 
+@pytest.mark.parametrize("name,new,cached,top_k,np_", [
+    ("decode", [1, 1, 1, 1], [3000, 200 * 128 + 5, 900 * 128, 40], 40, 0),
+    ("decode_split", [1, 1], [900 * 128, 3000 * 128 + 17], 64, 4),
+    ("spec", [3, 8, 1], [900 * 128, 150 * 128 + 9, 5000], 24, 0),
+])
+def test_selection_row_order_gives_bitwise_identical_results(name, new, cached, top_k, np_):
+    # The same selection written in another order (ids shuffled, the -1
+    # padding spread among them) is the same set of blocks: the decode rows
+    # then leave the in-order fast path for the bitmap, and every output must
+    # stay bit-identical to the indexer's ascending rows.
+    wl = wl_custom(f"roworder_{name}", new, cached, top_k=top_k, init=1, local=2, seed=41)
+    say(f"[case] {wl.name} np={np_}")
+    inp = I.make_inputs(wl, DEV)
+    d = B.run_indexer(inp)
+    o0 = B.run_attention(inp, d, num_partitions=np_).clone()
+    g = torch.Generator().manual_seed(7)
+    dp = d.cpu()
+    perm = torch.stack([torch.randperm(top_k, generator=g) for _ in range(dp.shape[0] * dp.shape[1])])
+    dp = torch.gather(dp.reshape(-1, top_k), 1, perm).reshape(dp.shape).contiguous()
+    assert not torch.equal(dp, d.cpu())
+    o1 = B.run_attention(inp, dp.to(DEV), num_partitions=np_)
+    torch.cuda.synchronize()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
 def test_page_permutation_gives_bitwise_identical_results():
     wl = wl_custom("perm", [1, 3], [7000, 2000], top_k=8)
     inp = I.make_inputs(wl, DEV)
