@@ -158,7 +158,7 @@ size_t indexer_ws(const msa_ragged& rg, int32_t num_kv_heads, int32_t top_k) {
 // ---- attention ---------------------------------------------------------------
 
 struct AttnPlan {
-  int tpw, ntg, np;
+  int tpw, ntg, np, tgs;
 };
 
 // Tokens per wave and waves (token groups) per workgroup of the decode
@@ -172,18 +172,36 @@ void decode_tiling(const msa_ragged& rg, int G, int* tpw, int* ntg, int* ntgb) {
   *ntgb = (ntok_groups + *ntg - 1) / *ntg;
 }
 
+// Speculative rows of two to four token groups, in one partition: one wave
+// per workgroup instead of one workgroup per (sequence, KV head).  A
+// workgroup of four token groups puts every wave of a sequence with many
+// draft tokens on one CU, and a CU streams at most about 43 GB/s however
+// many of its waves are busy; one-wave workgroups, the busy token groups
+// first, spread the busy waves over the CUs.  The waves still walk their
+// unions on one common schedule, each computing it from every token group's
+// selections.
+void one_wave_groups(Route r, int ntok_groups, AttnPlan* pl) {
+  pl->tgs = 1;
+  if (r == Route::Spec && pl->tpw > 1 && ntok_groups >= 2 && ntok_groups <= 4 && pl->np == 1) {
+    pl->ntg = 1;
+    pl->tgs = ntok_groups;
+  }
+}
+
 AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int req_np, int cus) {
   AttnPlan pl{};
   const Route r = route_of(rg);
   int ntgb = 0;
   decode_tiling(rg, G, &pl.tpw, &pl.ntg, &ntgb);
   const int ntok_groups = (rg.max_seq_length + pl.tpw - 1) / pl.tpw;
+  pl.tgs = 1;
   if (r == Route::Prefill) {
     pl.np = 1;
     return pl;
   }
   if (req_np > 0) {
     pl.np = req_np;
+    one_wave_groups(r, ntok_groups, &pl);
     return pl;
   }
   // CU fill.  Measured on the decode workloads: once the batch alone gives
@@ -201,6 +219,7 @@ AttnPlan plan_attention(const msa_ragged& rg, int G, int H_kv, int top_k, int re
     np = std::min<int64_t>(np, std::max(1, union_blocks / min_per));
   }
   pl.np = (int)std::max<int64_t>(1, std::min<int64_t>(np, kMaxPartitions));
+  one_wave_groups(r, ntok_groups, &pl);
   return pl;
 }
 
@@ -669,6 +688,7 @@ int attention_paged_entry(void* output, const void* q, const int32_t* d_indices,
   p.top_k = top_k;
   p.tpw = pl.tpw;
   p.ntg = pl.ntg;
+  p.tgs = pl.tgs;
   p.np = pl.np;
   p.rcap = (int32_t)row_capacity(*rg);
   p.nbmax = block_bound(*rg);

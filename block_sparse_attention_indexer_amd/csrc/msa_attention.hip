@@ -56,15 +56,55 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   // Group = (sequence, KV head, workgroup of token groups); its np
   // partitions are workgroups whose indices are congruent modulo the XCD
   // count, which the hardware dispatches to one XCD (workgroup i runs on XCD
-  // i mod 8), so that the split-K exchange stays inside one L2.
-  int pi, grp;
-  splitk_slot(blockIdx.x, p.np, &pi, &grp);
-  if (grp >= p.rg.batch * p.H_kv * ntgb) return;   // padding of the last XCD round
-  int x = grp;
-  const int tgb = x % ntgb;
-  x /= ntgb;
-  const int h = x % p.H_kv;
-  const int b = x / p.H_kv;
+  // i mod 8), so that the split-K exchange stays inside one L2.  With
+  // one-wave workgroups of p.tgs token groups (speculative rows, one
+  // partition), the token groups of a (sequence, KV head) are placed the
+  // same way, on one XCD, so that the blocks they share meet in its L2.
+  int pi, grp, tgb, sh;   // grp: split-K group (flags); sh: (sequence, KV head)
+  if (p.tgs > 1) {
+    // One-wave workgroups of speculative rows: XCD x takes the (sequence,
+    // KV head) pairs sh = 8 q + x, and its workgroup j the j-th token group
+    // that has tokens, counting q-major.  So the busy token groups are the
+    // XCD's first workgroups, which the dispatcher spreads over its CUs
+    // (consecutive workgroups go to different CUs), and the token groups of
+    // one pair sit on one XCD, side by side, where the blocks they share
+    // meet in its L2.  Workgroups past the busy token groups have nothing
+    // to do.
+    const int xcd = blockIdx.x % kXcdCount, j = blockIdx.x / kXcdCount;
+    const int pairs = p.rg.batch * p.H_kv;
+    int seen = 0;
+    sh = -1;
+    tgb = 0;
+    for (int q0 = 0; q0 * kXcdCount < pairs; q0 += 64) {
+      const int sq = (q0 + lane) * kXcdCount + xcd;
+      int act = 0;
+      if (sq < pairs) {
+        const int bq = sq / p.H_kv;
+        const int nq = min(p.rg.offs[bq + 1] - p.rg.offs[bq], p.rg.max_seq);
+        act = min(p.tgs, (max(nq, 0) + p.tpw - 1) / p.tpw);
+      }
+      int before = 0, total = 0;
+      wave_prefix_small(act, &before, &total);
+      const uint64_t hit = ballot(act > 0 && seen + before <= j && j < seen + before + act);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        sh = (q0 + l) * kXcdCount + xcd;
+        tgb = j - seen - __builtin_amdgcn_readlane(before, l);
+        break;
+      }
+      seen += total;
+    }
+    if (sh < 0) return;
+    pi = 0;
+    grp = sh;                                      // (one partition: no flags)
+  } else {
+    splitk_slot(blockIdx.x, p.np, &pi, &grp);
+    if (grp >= p.rg.batch * p.H_kv * ntgb) return;   // padding of the last XCD round
+    tgb = grp % ntgb;
+    sh = grp / ntgb;
+  }
+  const int h = sh % p.H_kv;
+  const int b = sh / p.H_kv;
 
   const int r0 = p.rg.offs[b];
   const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);   // keeps rows < rcap
@@ -77,10 +117,17 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   const int ntok = max(0, min(n - tok0, p.tpw));
 
   // ---- union of the wave's token selections, ascending, in LDS ----------
+  // LDS: one bitmap row of nbw words per token of the TG token groups
+  // scheduled together (the workgroup's waves, or with one-wave workgroups
+  // every token group of the (sequence, KV head)), then each wave's union.
   const int nbw = (p.nbmax + 31) >> 5;
   const int cap = p.tpw * p.top_k;
-  uint32_t* bm = lds + wave * (p.tpw * nbw + 2 * cap);
-  int32_t* uid = reinterpret_cast<int32_t*>(bm + p.tpw * nbw);
+  const int TG = W > 1 ? W : p.tgs;
+  const int own = W > 1 ? wave : tgb;              // this wave's token group among the TG
+  const int row_tok0 = W > 1 ? tgb * W * p.tpw : 0;   // token of bitmap row 0
+  uint32_t* bm = lds;
+  uint32_t* bm_own = bm + own * p.tpw * nbw;
+  int32_t* uid = reinterpret_cast<int32_t*>(lds + TG * p.tpw * nbw + wave * 2 * cap);
   uint32_t* umk = reinterpret_cast<uint32_t*>(uid + cap);
   int nU = 0;
   // One token per wave (decode): when the row's valid ids come first and
@@ -89,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   // umk (the token mask is 1), so the page lookup needs no round trip of its
   // own after the union is built.  Other rows take the bitmap below.
   bool ids_in_order = false;
-  if (p.tpw == 1 && W == 1 && ntok == 1) {
+  if (p.tpw == 1 && TG == 1 && ntok == 1) {
     const int nbt = min((c + tok0) / kBlock + 1, p.nbmax);
     const int32_t* lst = p.d_indices + ((size_t)(r0 + tok0) * p.H_kv + h) * p.top_k;
     bool ok = true, seen_invalid = false;
@@ -117,15 +164,20 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     if (!ok) nU = 0;
   }
   if (!ids_in_order) {
-    for (int i = lane; i < p.tpw * nbw; i += 64) bm[i] = 0u;
+    // rows this wave fills: its own token group's, or with one-wave
+    // workgroups every token group's
+    const int rw0 = W > 1 ? own * p.tpw : 0;
+    const int rw1 = W > 1 ? rw0 + p.tpw : TG * p.tpw;
+    for (int i = rw0 * nbw + lane; i < rw1 * nbw; i += 64) bm[i] = 0u;
     __syncthreads();
-    for (int tl = 0; tl < ntok; ++tl) {
-      const int tok = tok0 + tl;
+    for (int row = rw0; row < rw1; ++row) {
+      const int tok = row_tok0 + row;
+      if (tok >= n) break;
       const int nbt = min((c + tok) / kBlock + 1, p.nbmax);
       const int32_t* lst = p.d_indices + ((size_t)(r0 + tok) * p.H_kv + h) * p.top_k;
       for (int i = lane; i < p.top_k; i += 64) {
         const int id = lst[i];
-        if (id >= 0 && id < nbt) atomicOr(&bm[tl * nbw + (id >> 5)], 1u << (id & 31));
+        if (id >= 0 && id < nbt) atomicOr(&bm[row * nbw + (id >> 5)], 1u << (id & 31));
       }
     }
     __syncthreads();
@@ -142,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
         uint32_t u = 0u;
 #pragma unroll
         for (int tl = 0; tl < T; ++tl) {
-          wd[tl] = tl < ntok && w < nbw ? bm[tl * nbw + w] : 0u;
+          wd[tl] = tl < ntok && w < nbw ? bm_own[tl * nbw + w] : 0u;
           u |= wd[tl];
         }
         int before = 0, total = 0;
@@ -185,13 +237,13 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   // (the bit-sliced count takes four).  The order of blocks changes only
   // the rounding order of the softmax sums.
   if (p.tpw > 1 && nU > 1) {
-    if (W > 1 && W <= 4 && nU <= 64 && nbw <= 64) {
+    if (TG > 1 && TG <= 4 && nU <= 64 && nbw <= 64) {
       // -- blocks needed by exactly 2, 3 and 4 waves, per 32-block word --
       uint32_t E2 = 0u, E3 = 0u, E4 = 0u;
       if (lane < nbw) {
         uint32_t u[4] = {0u, 0u, 0u, 0u};
-        for (int w2 = 0; w2 < W; ++w2) {
-          const uint32_t* bm2 = lds + w2 * (p.tpw * nbw + 2 * cap);
+        for (int w2 = 0; w2 < TG; ++w2) {
+          const uint32_t* bm2 = bm + w2 * p.tpw * nbw;
           uint32_t any = 0u;
           for (int tl = 0; tl < p.tpw; ++tl) any |= bm2[tl * nbw + lane];
           u[w2] = any;
@@ -544,13 +596,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
 
 size_t attention_decode_lds_bytes(const AttnParams& p) {
   const int nbw = (p.nbmax + 31) / 32;
-  return (size_t)p.ntg * (p.tpw * nbw + 2 * p.tpw * p.top_k) * sizeof(uint32_t);
+  const int tg = p.ntg > 1 ? p.ntg : p.tgs;
+  return ((size_t)tg * p.tpw * nbw + (size_t)p.ntg * 2 * p.tpw * p.top_k) * sizeof(uint32_t);
 }
 
 hipError_t launch_attention_decode(const AttnParams& p, bool fp8, hipStream_t s) {
   const int ntok_groups = (p.rg.max_seq + p.tpw - 1) / p.tpw;
   const int ntgb = (ntok_groups + p.ntg - 1) / p.ntg;
-  const size_t nwg = splitk_workgroups((size_t)p.rg.batch * p.H_kv * ntgb, p.np);
+  const size_t nwg = p.tgs > 1 ? (size_t)kXcdCount * ((p.rg.batch * p.H_kv + kXcdCount - 1) / kXcdCount) * p.tgs
+                               : splitk_workgroups((size_t)p.rg.batch * p.H_kv * ntgb, p.np);
   const size_t lds = attention_decode_lds_bytes(p);
   dim3 grid((unsigned)nwg), block(64 * p.ntg);
   if (fp8) hipLaunchKernelGGL(attn_decode_kernel<true>, grid, block, lds, s, p);

@@ -62,6 +62,9 @@ struct AttnParams {
   int32_t H_q, H_kv, G, top_k;
   int32_t tpw;            // tokens per wave (decode / speculative route)
   int32_t ntg;            // token groups (waves) per workgroup
+  // token groups of one (sequence, KV head) that one-wave workgroups
+  // schedule together (speculative rows, one partition); 1 otherwise
+  int32_t tgs;
   int32_t np;             // split-K partitions
   int32_t rcap;           // rows of the partial buffers (batch * max_seq)
   int32_t nbmax;          // blocks a sequence may hold (bitmap size)

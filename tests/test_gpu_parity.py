@@ -108,6 +108,15 @@ def test_decode_fp8_long_full():
 
 # --- shape variants and edge cases -----------------------------------------
 
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_spec_one_partition_one_wave_workgroups(G):
+    # one partition: with 2 to 4 token groups per (sequence, KV head) each
+    # token group runs as its own one-wave workgroup, placed on its
+    # sequence's XCD, computing the common block schedule itself
+    run_and_check(wl_custom(f"g{G}_spec_np1", [3, 8, 1, 5, 2], [3000, 127, 5000, 2500, 90000], G=G,
+                            top_k=7), num_partitions=1)
+
+
 @pytest.mark.parametrize("G", [1, 2, 4, 16])
 def test_group_sizes_decode_and_spec(G):
     run_and_check(wl_custom(f"g{G}_decode", [1, 1, 1], [3000, 129, 5000], G=G))
@@ -180,8 +189,9 @@ def test_top_k_over_a_few_thousand_candidates():
                             top_k=100, init=2, local=3))
 
 
+@pytest.mark.parametrize("np_", [0, 1])
 @pytest.mark.parametrize("case", ["union64", "bitmap65", "mixed_paths"])
-def test_speculative_block_schedule_edges(case):
+def test_speculative_block_schedule_edges(case, np_):
     # The waves of a speculative (sequence, KV head) walk their unions on one
     # common schedule when a wave's union has at most 64 blocks and the block
     # bitmaps at most 64 words, else block 0 first and then newest first.
@@ -193,6 +203,9 @@ def test_speculative_block_schedule_edges(case):
     # mixed_paths: 40 picks per token, so some waves of a workgroup hold
     #   more than 64 blocks and take the fallback while the others follow
     #   the schedule.
+    # np_ = 0 lets the planner split these small batches (workgroups of the
+    # token groups of one (sequence, KV head)); np_ = 1 gives one-wave
+    # workgroups that each compute the schedule from every token group.
     if case == "union64":
         wl = wl_custom("sched_union64", [5, 6, 8, 3], [190000, 150000, 120000, 170000], H_kv=1,
                        top_k=32, init=0, local=0, seed=21)
@@ -202,7 +215,7 @@ def test_speculative_block_schedule_edges(case):
     else:
         wl = wl_custom("sched_mixed", [7, 4, 2], [100000, 50000, 9000], H_kv=2, top_k=40,
                        init=1, local=1, seed=23)
-    run_and_check(wl, chunk=1)
+    run_and_check(wl, chunk=1, num_partitions=np_)
 
 
 def test_two_column_groups_per_sequence():
