@@ -74,9 +74,15 @@ __device__ __forceinline__ int64_t group_units(const IndexerParams& p, int n, in
   return u;
 }
 
+// Sequences whose shape (new and cached tokens, first row) a scorer
+// workgroup keeps in LDS from its prefix pass, so that a segment's setup
+// needs no second round trip for them; larger batches read them again.
+constexpr int kSeqLds = 1024;
+
 template <int NCT, bool FP8>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParams p, int ncg) {
   __shared__ int64_t chunk_pre[kIdxThreads + 1];
+  __shared__ int3 seq_lds[kSeqLds];
   const int lane = threadIdx.x & 63;
   const int wave = uniform((int)(threadIdx.x >> 6));
   const int l16 = lane & 15, g = lane >> 4;
@@ -90,6 +96,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
     const int b_end = min(B, (int)(threadIdx.x + 1) * cpt);
     for (int b = threadIdx.x * cpt; b < b_end; ++b) {
       const int2 nc = seq_shape(p, b);
+      if (B <= kSeqLds) seq_lds[b] = int3{nc.x, nc.y, p.rg.offs[b]};
       if (nc.x > 0) u += group_units<NCT>(p, nc.x, nc.y, hpi, ncg) * p.H_ik;
     }
     for (int d = 1; d < 64; d <<= 1) {
@@ -127,14 +134,20 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
       if (chunk_pre[mid] <= s) lo = mid; else hi = mid;
     }
     // walk the chunk's sequences, then (hk, column group) inside the sequence
+    // (new tokens, cached tokens, first row) of sequence bq
+    auto shape = [&](int bq) {
+      if (B <= kSeqLds) return seq_lds[bq];
+      const int2 v = seq_shape(p, bq);
+      return int3{v.x, v.y, p.rg.offs[bq]};
+    };
     int64_t acc = chunk_pre[lo];
     int b = lo * cpt;
-    int2 nc = seq_shape(p, b);
+    int3 nc = shape(b);
     int64_t per_hk = nc.x > 0 ? group_units<NCT>(p, nc.x, nc.y, hpi, ncg) : 0;
     while (acc + per_hk * p.H_ik <= s) {
       acc += per_hk * p.H_ik;
       ++b;
-      nc = seq_shape(p, b);
+      nc = shape(b);
       per_hk = nc.x > 0 ? group_units<NCT>(p, nc.x, nc.y, hpi, ncg) : 0;
     }
     const int n = nc.x, c = nc.y;
@@ -152,7 +165,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerParam
     const int nblk = (int)min(min((int64_t)(gr.hi - blk_lo), e - s), (int64_t)kMaxSegment);
     s += nblk;
 
-    const int r0 = p.rg.offs[b];
+    const int r0 = nc.z;
     const int col0 = cg * 16 * NCT;
     u32x4 qf[NCT][4];
     int plim[NCT];     // last visible position of the column's token (-1: none)
