@@ -117,6 +117,16 @@ def test_spec_one_partition_one_wave_workgroups(G):
                             top_k=7), num_partitions=1)
 
 
+def test_spec_one_wave_workgroups_many_pairs():
+    # 72 sequences x 8 KV heads = 576 (sequence, KV head) pairs, 72 per XCD:
+    # a workgroup's search for its token group crosses a 64-pair chunk
+    g = np.random.default_rng(11)
+    new = [int(x) for x in g.integers(1, 9, size=72)]
+    cached = [int(x) for x in g.integers(200, 4000, size=72)]
+    run_and_check(wl_custom("spec_np1_many", new, cached, H_kv=8, G=8, top_k=6, seed=12),
+                  num_partitions=1, chunk=24)
+
+
 @pytest.mark.parametrize("G", [1, 2, 4, 16])
 def test_group_sizes_decode_and_spec(G):
     run_and_check(wl_custom(f"g{G}_decode", [1, 1, 1], [3000, 129, 5000], G=G))
