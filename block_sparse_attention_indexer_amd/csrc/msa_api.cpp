@@ -699,6 +699,11 @@ int attention_paged_entry(void* output, const void* q, const int32_t* d_indices,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (union_tiles) {
     const int waves = route == Route::Prefill ? kUnionWavesPrefill : kUnionWavesShared;
+    // Speculative rows (one tile per sequence and KV head, slots of similar
+    // size): each workgroup builds its slot's plan, with no plan or schedule
+    // launch.  The prefill route's many uneven slots keep the heaviest-first
+    // work list.
+    p.inline_plan = waves == kUnionWavesShared ? 1 : 0;
     int nct = 0;
     prefill_tiling(G, fp8, waves, &p.tq, &nct);
     p.ntiles = (rg->max_seq_length + p.tq - 1) / p.tq;

@@ -79,6 +79,10 @@ struct AttnParams {
   uint64_t epoch;         // per call, never 0
   // prefill route: tiles of tq tokens and the device-built plan
   int32_t tq, ntiles;     // tokens per tile, tiles per sequence
+  // union-tile kernel: one workgroup per slot that builds the slot's plan
+  // itself (no plan and schedule launches), or persistent workgroups over
+  // the work list
+  int32_t inline_plan;
   int32_t* plan_cnt;      // [B][ntiles][H_kv] union size
   int32_t* plan_ids;      // [B][ntiles][H_kv][nbmax] ascending block ids
   int32_t* plan_pages;    // [B][ntiles][H_kv][nbmax] page id of each block

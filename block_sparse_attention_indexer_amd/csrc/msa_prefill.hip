@@ -496,73 +496,84 @@ hipError_t launch_indexer_prefill(const IndexerParams& p, int num_cus, hipStream
 }
 
 // ---------------------------------------------------------------------------
-// Prefill plan: one wave per (sequence, tile, KV head).
+// Prefill plan of one (sequence, tile, KV head) slot, built by the calling
+// workgroup (any number of waves): the ascending union of the blocks the
+// tile's tokens selected, each block's page and the mask of the tokens that
+// chose it.  member: LDS of nbmax words (an LDS-space pointer, so that no
+// generic-pointer conversion is involved).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
-  extern __shared__ uint32_t member[];   // [nbmax] token mask per block
-  const int lane = threadIdx.x;
-  int x = blockIdx.x;
-  const int h = x % p.H_kv;
-  x /= p.H_kv;
-  const int tile = x % p.ntiles;
-  const int b = x / p.ntiles;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ void build_plan(const AttnParams& p, int b, int tile, int h, lds_u32* member) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const size_t slot = ((size_t)b * p.ntiles + tile) * p.H_kv + h;
   const int r0 = p.rg.offs[b];
   const int n = min(p.rg.offs[b + 1] - r0, p.rg.max_seq);
   const int t0 = tile * p.tq;
   if (t0 >= n) {
-    if (lane == 0) p.plan_cnt[slot] = 0;
+    if (tid == 0) p.plan_cnt[slot] = 0;
     return;
   }
   const int c = p.rg.clen[b];
   const int ntok = min(p.tq, n - t0);
   const int nb_last = min((c + t0 + ntok - 1) / kBlock + 1, p.nbmax);
   // more new tokens than the host bound, or blocks past the table (clipped)
-  if (lane == 0 && h == 0 &&
+  if (tid == 0 && h == 0 &&
       ((tile == 0 && p.rg.offs[b + 1] - r0 > p.rg.max_seq) || (c + t0 + ntok - 1) / kBlock >= p.nbmax))
     report_error(p.err, kErrLength);
-  for (int i = lane; i < nb_last; i += 64) member[i] = 0u;
+  for (int i = tid; i < nb_last; i += blockDim.x) member[i] = 0u;
   __syncthreads();
-  for (int tl = 0; tl < ntok; ++tl) {
+  for (int k = tid; k < ntok * p.top_k; k += blockDim.x) {
+    const int tl = k / p.top_k;
     const int nbt = min((c + t0 + tl) / kBlock + 1, p.nbmax);
-    const int32_t* lst = p.d_indices + ((size_t)(r0 + t0 + tl) * p.H_kv + h) * p.top_k;
-    for (int i = lane; i < p.top_k; i += 64) {
-      const int id = lst[i];
-      if (id >= 0 && id < nbt) atomicOr(&member[id], 1u << tl);
-    }
+    const int id = p.d_indices[((size_t)(r0 + t0 + tl) * p.H_kv + h) * p.top_k + k % p.top_k];
+    if (id >= 0 && id < nbt)
+      __hip_atomic_fetch_or(member + id, 1u << tl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
-  int32_t* ids = p.plan_ids + slot * p.nbmax;
-  int32_t* pgs = p.plan_pages + slot * p.nbmax;
-  uint32_t* msk = p.plan_mask + slot * p.nbmax;
-  const int32_t* trow = p.rg.table + (size_t)b * p.rg.stride;
-  int cnt = 0;
-  for (int base = 0; base < nb_last; base += 64) {
-    const int i = base + lane;
-    const uint32_t m = i < nb_last ? member[i] : 0u;
-    const uint64_t bal = ballot(m != 0u);
-    if (m) {
-      const int pos = cnt + mask_rank(bal);
-      const int pg = trow[i];
-      ids[pos] = i;
-      pgs[pos] = (unsigned)pg < (unsigned)p.k.num_pages ? pg : -1;
-      if ((unsigned)pg >= (unsigned)p.k.num_pages) report_error(p.err, kErrPage);
-      msk[pos] = m;
+  if (tid < 64) {   // the first wave compacts the union
+    int32_t* ids = p.plan_ids + slot * p.nbmax;
+    int32_t* pgs = p.plan_pages + slot * p.nbmax;
+    uint32_t* msk = p.plan_mask + slot * p.nbmax;
+    const int32_t* trow = p.rg.table + (size_t)b * p.rg.stride;
+    int cnt = 0;
+    for (int base = 0; base < nb_last; base += 64) {
+      const int i = base + lane;
+      const uint32_t m = i < nb_last ? member[i] : 0u;
+      const uint64_t bal = ballot(m != 0u);
+      if (m) {
+        const int pos = cnt + mask_rank(bal);
+        const int pg = trow[i];
+        ids[pos] = i;
+        pgs[pos] = (unsigned)pg < (unsigned)p.k.num_pages ? pg : -1;
+        if ((unsigned)pg >= (unsigned)p.k.num_pages) report_error(p.err, kErrPage);
+        msk[pos] = m;
+      }
+      cnt += __popcll(bal);
     }
-    cnt += __popcll(bal);
-  }
-  if (lane == 0) p.plan_cnt[slot] = cnt;
-  if (cnt == 0) {
-    // No token of the tile has a visible block: the work list holds
-    // non-empty slots only, so the tile's rows of this head group get their
-    // result, 0, here.  256-byte rows, written as 16-byte pieces.
-    const int pieces = ntok * p.G * (kDim * 2 / 16);
-    for (int i = lane; i < pieces; i += 64) {
-      const int row = i / (p.G * 16), head = (i / 16) % p.G, col = i % 16;
-      uint16_t* op = p.out + ((size_t)(r0 + t0 + row) * p.H_q + h * p.G + head) * kDim + 8 * col;
-      *reinterpret_cast<u32x4*>(op) = u32x4{0u, 0u, 0u, 0u};
+    if (lane == 0) p.plan_cnt[slot] = cnt;
+    if (cnt == 0) {
+      // No token of the tile has a visible block: the work list holds
+      // non-empty slots only, so the tile's rows of this head group get
+      // their result, 0, here.  256-byte rows, written as 16-byte pieces.
+      const int pieces = ntok * p.G * (kDim * 2 / 16);
+      for (int i = lane; i < pieces; i += 64) {
+        const int row = i / (p.G * 16), head = (i / 16) % p.G, col = i % 16;
+        uint16_t* op = p.out + ((size_t)(r0 + t0 + row) * p.H_q + h * p.G + head) * kDim + 8 * col;
+        *reinterpret_cast<u32x4*>(op) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
+}
+
+// Prefill plan launch: one wave per (sequence, tile, KV head).
+__global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
+  extern __shared__ uint32_t member[];   // [nbmax] token mask per block
+  int x = blockIdx.x;
+  const int h = x % p.H_kv;
+  x /= p.H_kv;
+  const int tile = x % p.ntiles;
+  const int b = x / p.ntiles;
+  build_plan(p, b, tile, h, (lds_u32*)member);
 }
 
 constexpr int kRingHalf = 256;   // plan entries per half of the LDS ring
@@ -967,15 +978,31 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   }
 }
 
-template <bool FP8, int NCT, int W>
+// INLINE: one workgroup per slot, which first builds the slot's plan itself
+// (in the K ring, free until the tile's first DMA; nbmax words fit in it).
+// Otherwise persistent workgroups over the work list.  (Two instantiations
+// rather than a run-time choice: with both paths in one kernel the compiler
+// emits an invalid instruction.)
+template <bool FP8, int NCT, int W, bool INLINE>
 __global__ __launch_bounds__(64 * W) void attn_prefill3_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) PrefillLds3 lds;
-  __shared__ int item_s;
-  const int xcd = xcd_id();
-  for (;;) {
-    const int slot = take_slot_xcd(p.sched, p.worklist, xcd, &item_s);
-    if (slot < 0) break;
+  if constexpr (INLINE) {
+    const int slot = (int)blockIdx.x;
+    int x = slot;
+    const int h = x % p.H_kv;
+    x /= p.H_kv;
+    const int tile = x % p.ntiles;
+    build_plan(p, x / p.ntiles, tile, h, (lds_u32*)lds.k);
+    __syncthreads();
     attn_prefill3_tile<FP8, NCT, W>(p, slot, lds);
+  } else {
+    __shared__ int item_s;
+    const int xcd = xcd_id();
+    for (;;) {
+      const int slot = take_slot_xcd(p.sched, p.worklist, xcd, &item_s);
+      if (slot < 0) break;
+      attn_prefill3_tile<FP8, NCT, W>(p, slot, lds);
+    }
   }
 }
 
@@ -990,20 +1017,22 @@ void prefill_tiling(int G, bool /*fp8*/, int waves, int* tq, int* nct) {
 
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hipStream_t s) {
   const size_t slots = (size_t)p.rg.batch * p.ntiles * p.H_kv;
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3((unsigned)slots), dim3(64),
-                     (size_t)p.nbmax * sizeof(uint32_t), s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)p.nwg), block(64 * waves);
-  if (waves == kUnionWavesShared) {
-    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1, kUnionWavesShared>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1, kUnionWavesShared>), grid, block, 0, s, p);
+  if (!p.inline_plan) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3((unsigned)slots), dim3(64),
+                       (size_t)p.nbmax * sizeof(uint32_t), s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(p.inline_plan ? slots : (size_t)p.nwg)), block(64 * waves);
+  if (p.inline_plan) {   // the speculative rows' workgroups of kUnionWavesShared waves
+    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1, kUnionWavesShared, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1, kUnionWavesShared, true>), grid, block, 0, s, p);
   } else {
-    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1, kUnionWavesPrefill>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1, kUnionWavesPrefill>), grid, block, 0, s, p);
+    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 1, kUnionWavesPrefill, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 1, kUnionWavesPrefill, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
