@@ -56,10 +56,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
   // Group = (sequence, KV head, workgroup of token groups); its np
   // partitions are workgroups whose indices are congruent modulo the XCD
   // count, which the hardware dispatches to one XCD (workgroup i runs on XCD
-  // i mod 8), so that the split-K exchange stays inside one L2.  With
-  // one-wave workgroups of p.tgs token groups (speculative rows, one
-  // partition), the token groups of a (sequence, KV head) are placed the
-  // same way, on one XCD, so that the blocks they share meet in its L2.
+  // i mod 8), so that the split-K exchange stays inside one L2.  One-wave
+  // workgroups of speculative rows (p.tgs > 1, one partition) keep the
+  // token groups of a (sequence, KV head) on one XCD as well (below).
   int pi, grp, tgb, sh;   // grp: split-K group (flags); sh: (sequence, KV head)
   if (p.tgs > 1) {
     // One-wave workgroups of speculative rows: XCD x takes the (sequence,
