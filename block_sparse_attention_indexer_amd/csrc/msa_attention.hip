@@ -20,6 +20,13 @@
 // so the softmax statistics of a column stay in the lanes that own it and
 // no LDS round trip is needed.  Online softmax runs per 64-position half
 // block in log2 units.
+//
+// Workgroups: one wave per (sequence, KV head) on the decode route; the
+// token groups of a (sequence, KV head) in one workgroup when speculative
+// rows are split into partitions; and one wave per workgroup, the busy
+// token groups first, when speculative rows run in one partition (a CU
+// streams at most about 43 GB/s however many of its waves are busy, so the
+// busy waves are spread over the CUs).
 #include <type_traits>
 
 #include "msa_common.h"
