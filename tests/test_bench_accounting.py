@@ -157,3 +157,53 @@ def test_more_than_one_gpu_is_refused_before_any_device_call():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_counter_rows_are_summed_per_dispatch(tmp_path):
+    # rocprofv3 reports a counter once per instance (e.g. per XCD) of a
+    # dispatch; the record takes the sum per dispatch, per kernel
+    rows = [("copyBuffer", 1, "FETCH_SIZE", 100.0), ("copyBuffer", 1, "FETCH_SIZE", 28.0),
+            ("msa::attn_decode_kernel<false>", 2, "FETCH_SIZE", 5.0),
+            ("msa::attn_decode_kernel<false>", 2, "FETCH_SIZE", 7.0),
+            ("msa::attn_decode_kernel<false>", 3, "FETCH_SIZE", 11.0),
+            ("msa::attn_decode_kernel<false>", 3, "WRITE_SIZE", 99.0)]
+    path = tmp_path / "run_counter_collection.csv"
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for k, d, c, v in rows:
+            f.write(f'{d},"{k}",{c},{v}\n')
+    per = bench._counter_per_dispatch(str(path), "FETCH_SIZE")
+    assert per == {"copyBuffer": [128.0], "msa::attn_decode_kernel<false>": [12.0, 11.0]}
+    assert bench._counter_per_dispatch(str(path), "WRITE_SIZE") == {"msa::attn_decode_kernel<false>": [99.0]}
+
+
+def traffic_records():
+    out = []
+    for f in sorted(os.listdir(bench.PROFILES)):
+        if f.endswith("_traffic.json"):
+            out.append(f)
+    return out
+
+
+@pytest.mark.parametrize("fname", traffic_records())
+def test_traffic_records_are_consistent(fname, monkeypatch):
+    """A committed record's HBM bytes are its two counters (KiB per launch)
+    scaled by the calibration copy's readings, and bench.py uses the record
+    only while the kernel sources hash to the value stored in it."""
+    import json
+    rec = json.load(open(os.path.join(bench.PROFILES, fname)))
+    cal = rec["calibration"]
+    hbm = (rec["fetch_size_kib_per_launch"] * 1024 * cal["fetch_scale"] +
+           rec["write_size_kib_per_launch"] * 1024 * cal["write_scale"])
+    assert abs(rec["hbm_bytes_per_launch"] - hbm) <= 1
+    assert rec["hbm_over_algorithmic"] == pytest.approx(
+        rec["hbm_bytes_per_launch"] / rec["algorithmic_gathered_kv_bytes_per_launch"], rel=1e-6)
+    # the calibration: a 1 GiB copy reads FETCH_SIZE KiB and writes WRITE_SIZE KiB
+    assert 0.5 <= cal["fetch_scale"] <= 4 and 0.5 <= cal["write_scale"] <= 4
+    kernel = fname.split("_traffic.json")[0]
+    workload = next(w for w in list(I.WORKLOADS) + ["spec_decode_reuse", "latent_decode", "latent_decode_fp8"]
+                    if kernel.endswith("_" + w) and kernel[:-len(w) - 1] == bench.kernel_of(w))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w=workload: rec["kernel_source_sha256_16"])
+    assert bench.traffic_record(workload) == rec["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w=workload: "0" * 16)
+    assert bench.traffic_record(workload) is None
