@@ -89,6 +89,11 @@ struct AttnParams {
   uint32_t* plan_mask;    // [B][ntiles][H_kv][nbmax] token mask per block
   int32_t* worklist;      // [B * ntiles * H_kv] non-empty plan slots, one list per XCD
   int32_t* sched;         // kSchedInts: per XCD list, its length, next entry and start
+  // dense-causal tiles (every token chose every block it sees): a second
+  // work list for the dense-tile kernel, or null when every slot goes to the
+  // list above
+  int32_t* dense_list;
+  int32_t* dense_sched;
   int32_t nwg;            // persistent workgroups launched
   uint32_t* err;          // device error word (bad table data), or null
 };
@@ -117,6 +122,8 @@ constexpr int kSchedInts = 24;
 // Waves of the union-tile attention kernel per workgroup: the prefill route,
 // and speculative rows whose sequences share one selection.
 constexpr int kUnionWavesPrefill = 16;
+constexpr int kUnionWavesDense = 8;     // dense-causal tiles: 8 waves x 32 columns
+constexpr int32_t kPlanDense = 1 << 30; // plan_cnt flag of a dense-causal slot
 constexpr int kUnionWavesShared = 4;
 hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hipStream_t s);
 

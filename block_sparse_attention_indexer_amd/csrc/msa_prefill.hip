@@ -536,9 +536,16 @@ __device__ void build_plan(const AttnParams& p, int b, int tile, int h, lds_u32*
     uint32_t* msk = p.plan_mask + slot * p.nbmax;
     const int32_t* trow = p.rg.table + (size_t)b * p.rg.stride;
     int cnt = 0;
+    // dense-causal: every token chose every block it sees (block i is seen
+    // by tokens c + t0 + tl >= 128 i of the tile)
+    const uint32_t all_tok = ntok >= 32 ? ~0u : (1u << ntok) - 1u;
+    bool dense = true;
     for (int base = 0; base < nb_last; base += 64) {
       const int i = base + lane;
       const uint32_t m = i < nb_last ? member[i] : 0u;
+      const int lo = min(31, max(0, i * kBlock - (c + t0)));
+      const uint32_t seen = i < nb_last ? all_tok & ~((1u << lo) - 1u) : 0u;
+      dense = dense && ballot(m != seen) == 0;
       const uint64_t bal = ballot(m != 0u);
       if (m) {
         const int pos = cnt + mask_rank(bal);
@@ -550,7 +557,7 @@ __device__ void build_plan(const AttnParams& p, int b, int tile, int h, lds_u32*
       }
       cnt += __popcll(bal);
     }
-    if (lane == 0) p.plan_cnt[slot] = cnt;
+    if (lane == 0) p.plan_cnt[slot] = cnt | (dense && cnt > 0 ? kPlanDense : 0);
     if (cnt == 0) {
       // No token of the tile has a visible block: the work list holds
       // non-empty slots only, so the tile's rows of this head group get
@@ -578,18 +585,32 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
 
 constexpr int kRingHalf = 256;   // plan entries per half of the LDS ring
 
+// One work list, or (dense_list set) one for the dense-causal slots and one
+// for the rest.
 __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams p) {
   __shared__ int hist[kXcds * kXcdBuckets];
-  schedule_by_xcd(p.rg.batch * p.ntiles, p.H_kv, p.nbmax, [&](int i) { return p.plan_cnt[i]; },
-                  p.worklist, p.sched, hist);
+  const int nbt = p.rg.batch * p.ntiles;
+  if (p.dense_list) {
+    schedule_by_xcd(nbt, p.H_kv, p.nbmax,
+                    [&](int i) { const int c = p.plan_cnt[i]; return (c & kPlanDense) ? c & (kPlanDense - 1) : 0; },
+                    p.dense_list, p.dense_sched, hist);
+    __syncthreads();
+    schedule_by_xcd(nbt, p.H_kv, p.nbmax,
+                    [&](int i) { const int c = p.plan_cnt[i]; return (c & kPlanDense) ? 0 : c; },
+                    p.worklist, p.sched, hist);
+  } else {
+    schedule_by_xcd(nbt, p.H_kv, p.nbmax, [&](int i) { return p.plan_cnt[i] & (kPlanDense - 1); },
+                    p.worklist, p.sched, hist);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Prefill attention with direct global->LDS tile loads, BF16 or FP8 KV.
 //
-// Workgroup = W waves (16 on the prefill route, four per SIMD; 4 for the
-// speculative rows of msa_attention_paged_shared), persistent over the slot
-// work list;
+// Workgroup = W waves (16 on the prefill route, four per SIMD; 8 of two
+// column tiles each for the prefill route's dense-causal slots, two per
+// SIMD; 4 for the speculative rows of msa_attention_paged_shared),
+// persistent over the slot work list;
 // wave w owns columns [w cpw, (w + 1) cpw) of the tile's tq * G (token,
 // query head) columns, as 16 * NCT MFMA columns.  K and V tiles are DMA'd
 // straight into LDS, row-major (256-byte rows for BF16, 128-byte rows for
@@ -651,7 +672,7 @@ __device__ void attn_prefill3_tile(const AttnParams& p, int slot, PrefillLds3& L
   const int c = p.rg.clen[b];
   const int ntok = min(p.tq, n - t0);
   const int p_tile_max = c + t0 + ntok - 1;
-  const int cnt = p.plan_cnt[slot];
+  const int cnt = p.plan_cnt[slot] & (kPlanDense - 1);
   const int32_t* ids = p.plan_ids + (size_t)slot * p.nbmax;
   const int32_t* pgs = p.plan_pages + (size_t)slot * p.nbmax;
   const uint32_t* msks = p.plan_mask + (size_t)slot * p.nbmax;
@@ -1010,7 +1031,9 @@ void prefill_tiling(int G, bool /*fp8*/, int waves, int* tq, int* nct) {
   // `waves` waves of at most 16 columns (one MFMA column tile), both KV
   // types.  Two column tiles per wave do not fit the 128 VGPRs a wave of a
   // 16-wave workgroup has: they spill inside the block loop (measured at
-  // group size 16: 32.6 ms against 11.3 ms with 16-token tiles).
+  // group size 16: 32.6 ms against 11.3 ms with 16-token tiles).  The
+  // dense-causal kernel (8 waves of two column tiles) takes the same tiles:
+  // 8 * 32 / G tokens = 256 / G.
   *tq = std::min(32, waves * 16 / G);
   *nct = 1;
 }
@@ -1024,6 +1047,17 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hi
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.dense_list) {
+    // the dense-causal slots first, by their own kernel and work list
+    AttnParams pd = p;
+    pd.worklist = p.dense_list;
+    pd.sched = p.dense_sched;
+    const dim3 dgrid((unsigned)p.nwg), dblock(64 * kUnionWavesDense);
+    if (fp8) hipLaunchKernelGGL((attn_prefill3_kernel<true, 2, kUnionWavesDense, false>), dgrid, dblock, 0, s, pd);
+    else hipLaunchKernelGGL((attn_prefill3_kernel<false, 2, kUnionWavesDense, false>), dgrid, dblock, 0, s, pd);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(p.inline_plan ? slots : (size_t)p.nwg)), block(64 * waves);

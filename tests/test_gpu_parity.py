@@ -440,6 +440,45 @@ def test_prefill_group_sizes(G):
                   per_seq=30)
 
 
+@pytest.mark.parametrize("G,kv", [(8, "bf16"), (16, "bf16"), (8, "fp8_e4m3")])
+def test_prefill_dense_and_sparse_tiles(G, kv):
+    # sequences 0 and 1 see at most top-k blocks (dense-causal tiles, which
+    # run on their own kernel at G = 8 and 16), sequence 2 sees 32-34 (sparse
+    # tiles); the tiles of the call are split between the two kernels
+    run_and_check(wl_custom(f"prefill_dense_mix_g{G}_{kv}", [200, 64, 300], [0, 900, 4000], G=G,
+                            top_k=8, kv=kv), per_seq=None)
+
+
+def test_prefill_short_context_selection_with_holes():
+    # A caller's selection may leave out visible blocks even where top-k
+    # covers them all: such tiles are not dense-causal.  Ids in another
+    # order and -1 slots; the output must follow the ids given.
+    wl = wl_custom("prefill_holes", [150, 90], [100, 600], top_k=8)
+    say(f"[case] {wl.name}")
+    inp = I.make_inputs(wl, DEV)
+    d = B.run_indexer(inp)
+    torch.cuda.synchronize()
+    d_cpu = d.cpu().numpy().copy()
+    rng = np.random.default_rng(5)
+    for r in range(d_cpu.shape[0]):
+        for h in range(d_cpu.shape[1]):
+            row = d_cpu[r, h]
+            valid = row[row >= 0]
+            if r % 3 == 0 and len(valid) > 1:      # drop one chosen block
+                valid = np.delete(valid, rng.integers(len(valid)))
+            row[:] = -1
+            row[:len(valid)] = rng.permutation(valid)
+    d_mod = torch.from_numpy(d_cpu).to(DEV)
+    out = B.run_attention(inp, d_mod)
+    torch.cuda.synchronize()
+    pb, orig_rows = O.problem_for_sequences(inp, list(range(wl.batch)))
+    rows = np.arange(len(orig_rows))
+    ref = O.attention(pb, d_cpu[orig_rows], rows)
+    err = parity.check_attention(out[torch.as_tensor(orig_rows, device=DEV)], ref, wl.kv_dtype,
+                                 wl.name)
+    say(f"  max|err|={err:.3e}")
+
+
 def test_prefill_fp8_kv():
     run_and_check(wl_custom("prefill_fp8", [70, 33], [2500, 0], kv="fp8_e4m3", top_k=7, local=3),
                   per_seq=30)
