@@ -354,6 +354,21 @@ def _counter_per_dispatch(path, counter):
     return out
 
 
+def call_counter_kib(per, workload):
+    """One attention call's counter value from {kernel name: [value per
+    dispatch]}: the mean per dispatch of every instance of the call's kernel
+    (the prefill route runs its dense-causal tiles on a second instance),
+    summed, plus the mean of each of the call's other kernels.  Returns
+    (per call, dispatches of the kernel, the other kernels' part)."""
+    inst = {name: vals for name, vals in per.items() if kernel_of(workload) in name}
+    extra = 0.0
+    for k in call_extra_kernels(workload):
+        vals = [v for name, vs in per.items() if k in name for v in vs]
+        extra += float(np.mean(vals)) if vals else 0.0
+    total = float(sum(np.mean(vals) for vals in inst.values())) + extra
+    return total, sum(len(v) for v in inst.values()), extra
+
+
 def write_traffic_record(args):
     """HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch) scaled by what the same counters read for the 1 GiB
@@ -369,18 +384,11 @@ def write_traffic_record(args):
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         per = _counter_per_dispatch(path, counter)
         copy = max(v for name, vals in per.items() if "copy" in name.lower() for v in vals)
-        attn = [v for name, vals in per.items() if kernel_of(args.workload) in name for v in vals]
-        if not attn:
+        per_call, ndisp, extra = call_counter_kib(per, args.workload)
+        if not ndisp:
             raise SystemExit(f"no {kernel_of(args.workload)} dispatch in {path}")
-        # the call's other kernels (the combine when split; the plan and
-        # schedule kernels of the union-tile route)
-        extra = 0.0
-        for k in call_extra_kernels(args.workload):
-            vals = [v for name, vs in per.items() if k in name for v in vs]
-            extra += float(np.mean(vals)) if vals else 0.0
         scale = COPY_BYTES / (copy * 1024.0)
-        per_call = float(np.mean(attn)) + extra
-        raw[counter] = (per_call, copy, scale, len(attn), extra)
+        raw[counter] = (per_call, copy, scale, ndisp, extra)
         scaled[counter] = per_call * 1024.0 * scale
 
     if is_latent(args.workload):

@@ -177,6 +177,18 @@ def test_counter_rows_are_summed_per_dispatch(tmp_path):
     assert bench._counter_per_dispatch(str(path), "WRITE_SIZE") == {"msa::attn_decode_kernel<false>": [99.0]}
 
 
+def test_call_counter_sums_every_instance_of_the_call_kernel():
+    # the prefill route launches two instances of the union-tile kernel per
+    # call (dense-causal tiles, then the rest) besides its plan and schedule
+    per = {"copyBuffer": [1000.0],
+           "msa::attn_prefill3_kernel<false, 2, 8, false>": [10.0, 12.0],
+           "msa::attn_prefill3_kernel<false, 1, 16, false>": [100.0, 102.0],
+           "msa::prefill_plan_kernel": [1.0, 3.0], "msa::attn_schedule_kernel": [2.0, 2.0]}
+    assert bench.call_counter_kib(per, "prefill_ragged") == (11.0 + 101.0 + 2.0 + 2.0, 4, 4.0)
+    per = {"msa::attn_decode_kernel<true>": [5.0, 7.0], "copyBuffer": [1.0]}
+    assert bench.call_counter_kib(per, "decode_fp8_long") == (6.0, 2, 0.0)
+
+
 def traffic_records():
     out = []
     for f in sorted(os.listdir(bench.PROFILES)):
