@@ -585,19 +585,20 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnParams p) {
 
 constexpr int kRingHalf = 256;   // plan entries per half of the LDS ring
 
-// One work list, or (dense_list set) one for the dense-causal slots and one
-// for the rest.
+// One work list, or (dense_list set; two workgroups) one for the
+// dense-causal slots, built by workgroup 1, and one for the rest.
 __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(AttnParams p) {
   __shared__ int hist[kXcds * kXcdBuckets];
   const int nbt = p.rg.batch * p.ntiles;
   if (p.dense_list) {
-    schedule_by_xcd(nbt, p.H_kv, p.nbmax,
-                    [&](int i) { const int c = p.plan_cnt[i]; return (c & kPlanDense) ? c & (kPlanDense - 1) : 0; },
-                    p.dense_list, p.dense_sched, hist);
-    __syncthreads();
-    schedule_by_xcd(nbt, p.H_kv, p.nbmax,
-                    [&](int i) { const int c = p.plan_cnt[i]; return (c & kPlanDense) ? 0 : c; },
-                    p.worklist, p.sched, hist);
+    if (blockIdx.x == 1)
+      schedule_by_xcd(nbt, p.H_kv, p.nbmax,
+                      [&](int i) { const int c = p.plan_cnt[i]; return (c & kPlanDense) ? c & (kPlanDense - 1) : 0; },
+                      p.dense_list, p.dense_sched, hist);
+    else
+      schedule_by_xcd(nbt, p.H_kv, p.nbmax,
+                      [&](int i) { const int c = p.plan_cnt[i]; return (c & kPlanDense) ? 0 : c; },
+                      p.worklist, p.sched, hist);
   } else {
     schedule_by_xcd(nbt, p.H_kv, p.nbmax, [&](int i) { return p.plan_cnt[i] & (kPlanDense - 1); },
                     p.worklist, p.sched, hist);
@@ -1045,7 +1046,7 @@ hipError_t launch_attention_prefill(const AttnParams& p, bool fp8, int waves, hi
                        (size_t)p.nbmax * sizeof(uint32_t), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(p.dense_list ? 2 : 1), dim3(kSchedThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
