@@ -449,6 +449,15 @@ def test_prefill_dense_and_sparse_tiles(G, kv):
                             top_k=8, kv=kv), per_seq=None)
 
 
+@pytest.mark.parametrize("G", [8, 16])
+def test_prefill_dense_causal_long_unions(G):
+    # every token sees 501..504 blocks and chooses them all (top-k 512):
+    # dense-causal tiles whose unions refill the kernel's LDS ring of plan
+    # entries, on the 8-wave kernel
+    run_and_check(wl_custom(f"prefill_dense_long_g{G}", [300], [64000], H_kv=1, G=G,
+                            top_k=B.MSA_MAX_TOPK, init=1, local=4), per_seq=4)
+
+
 def test_prefill_short_context_selection_with_holes():
     # A caller's selection may leave out visible blocks even where top-k
     # covers them all: such tiles are not dense-causal.  Ids in another
