@@ -584,19 +584,19 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnParams p) {
     }
     if (g == 0) p.part_lse[(size_t)pi * pstride + col] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
   }
-  bool poisoned = false;
-  __shared__ int timed_out;
-  if (!splitk_arrive(p.ready + (size_t)grp * p.np, pi, p.np, p.epoch, &poisoned, &timed_out)) return;
+  __shared__ int merge_sh[3];
+  uint64_t* flags = p.ready + (size_t)grp * p.np;
+  if (!splitk_arrive(flags, pi, p.np, p.epoch)) return;
   // each wave merges its own columns: l16 < nc (columns are token-major)
   const int nc = min(16, ntok * p.G);
   const int ncp = nc <= 2 ? 2 : nc <= 4 ? 4 : nc <= 8 ? 8 : 16;
   auto row_of = [&](int cc) { return r0 + tok0 + cc / p.G; };
   auto head_of = [&](int cc) { return h * p.G + cc % p.G; };
   switch (ncp) {
-    case 2: splitk_merge<1>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
-    case 4: splitk_merge<2>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
-    case 8: splitk_merge<4>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
-    default: splitk_merge<8>(p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane, poisoned); break;
+    case 2: splitk_merge<1>(flags, p.epoch, merge_sh, p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane); break;
+    case 4: splitk_merge<2>(flags, p.epoch, merge_sh, p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane); break;
+    case 8: splitk_merge<4>(flags, p.epoch, merge_sh, p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane); break;
+    default: splitk_merge<8>(flags, p.epoch, merge_sh, p.part_o, p.part_lse, p.out, p.H_q, p.rcap, p.np, nc, row_of, head_of, lane); break;
   }
 }
 

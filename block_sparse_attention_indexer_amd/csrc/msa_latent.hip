@@ -537,14 +537,13 @@ __global__ __launch_bounds__(64 * kLatWaves, 1) void latent_attn_kernel(LatentPa
   if (p.np_total == 1) return;
   // split-K: the group's last partition merges the partials of its (up to)
   // 64 query heads, 4 threads per head
-  bool poisoned = false;
-  // (the wave-merge statistics are dead past the arrival's first barrier)
-  if (!splitk_arrive(p.ready + (size_t)grp * p.np_total, gpi, p.np_total, p.epoch, &poisoned,
-                     reinterpret_cast<int*>(stat)))
-    return;
+  uint64_t* flags = p.ready + (size_t)grp * p.np_total;
+  if (!splitk_arrive(flags, gpi, p.np_total, p.epoch)) return;
   const int nc = min(64, p.G - cg * 64);
-  splitk_merge<8>(p.part_o, p.part_lse, p.out, p.H, p.rcap, p.np_total, nc, [&](int) { return r; },
-                  [&](int c) { return hl * p.G + cg * 64 + c; }, tid, poisoned);
+  // (the wave-merge statistics are dead past the arrival's barrier)
+  splitk_merge<8>(flags, p.epoch, reinterpret_cast<int*>(stat), p.part_o, p.part_lse, p.out, p.H,
+                  p.rcap, p.np_total, nc, [&](int) { return r; },
+                  [&](int c) { return hl * p.G + cg * 64 + c; }, tid);
 }
 
 template <bool FP8>

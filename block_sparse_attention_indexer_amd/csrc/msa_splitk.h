@@ -12,9 +12,11 @@
 // be the point where the partitions meet: partials are ordinary stores (the
 // vector L1 writes through to L2) whose completion a wave waits for before
 // it raises its flag; flags are set and polled with atomics, which execute
-// at L2; the merger reads the partials with ordinary loads, which its L1
-// cannot serve from a stale line because no workgroup reads a partial before
-// its merger does.  (A device-scope fence would instead write back and
+// at L2; the merger reads the partial outputs with ordinary loads, which
+// its L1 cannot serve from a stale line because no workgroup reads a
+// partial output before its merger does (a column's 512 bytes share no
+// cache line with another column), and the log-sum-exps, which do share
+// lines between groups, with L2-coherent loads.  (A device-scope fence would instead write back and
 // invalidate the whole L2 of the XCD; coherent cross-XCD stores and loads
 // would go to memory behind the kernel's own streaming traffic.)
 //
@@ -55,13 +57,9 @@ inline size_t splitk_workgroups(size_t groups, int np) {
 }
 
 // Called by every thread of the workgroup once its partial stores are
-// issued.  Returns false on the partitions that only contribute (they have
-// raised their flag and may exit), true on the merger once every other
-// partition's flag is up; *poisoned is then true if the wait gave up.
-// timed_out: one LDS int the caller no longer uses (written after the first
-// barrier here).
-__device__ __forceinline__ bool splitk_arrive(uint64_t* flags, int pi, int np, uint64_t epoch,
-                                              bool* poisoned, int* timed_out) {
+// issued.  The partitions that only contribute raise their flag and get
+// false (they may exit); the merger gets true and waits in splitk_merge.
+__device__ __forceinline__ bool splitk_arrive(uint64_t* flags, int pi, int np, uint64_t epoch) {
   __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
   __syncthreads();                 // ... and every wave's
   if (pi != np - 1) {
@@ -69,63 +67,86 @@ __device__ __forceinline__ bool splitk_arrive(uint64_t* flags, int pi, int np, u
       __hip_atomic_exchange(flags + pi, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
   }
-  if (threadIdx.x < 64) {
-    // wave 0: lane k watches partition k's flag (np <= 64)
-    const bool mine = (int)threadIdx.x < np - 1;
-    bool late = true;
-    for (int spin = 0; spin < (1 << 20); ++spin) {
-      const uint64_t f = mine ? __hip_atomic_fetch_or(flags + threadIdx.x, 0ull, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                              : epoch;
-      if (__builtin_amdgcn_ballot_w64(f != epoch) == 0) {
-        late = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    if (mine) __hip_atomic_exchange(flags + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) *timed_out = late;
-  }
-  __syncthreads();
-  *poisoned = *timed_out != 0;
   return true;
 }
 
-// Merge of a group's split-K partials: out = sum_pi exp(lse_pi - M) o_pi /
-// sum_pi exp(lse_pi - M) over the np partitions, in partition order
-// (deterministic whichever partition merges); lse = -inf carries no weight.
-// The group's nc columns (row col_row(c), head col_head(c)) are spread
-// over the nthreads threads: 32 / CH threads per column, each taking CH
-// chunks of 4 consecutive dims.  Partitions are read KB = 32 / CH at a
-// time, every load of a batch in flight together, with a running maximum
-// (the sums so far are rescaled when a batch raises it).
+// The merger's view of the other partitions' flags (wave 0: lane k watches
+// partition k, np <= 64), shared through LDS: with wait set, spins until
+// every flag is up and clears them (bounded: sh[2] is then set instead of
+// the wait never ending); else one look.  Bit k of the result: partition k
+// is done (the merger's own bit and bits >= np are set).  Every thread
+// calls it.
+__device__ __forceinline__ uint64_t splitk_flags(uint64_t* flags, int np, uint64_t epoch, bool wait,
+                                                 int* sh) {
+  if (threadIdx.x < 64) {
+    const bool mine = (int)threadIdx.x < np - 1;
+    uint64_t done = 0ull;
+    bool late = wait;
+    for (int spin = 0; spin < (wait ? (1 << 20) : 1); ++spin) {
+      const uint64_t f = mine ? __hip_atomic_fetch_or(flags + threadIdx.x, 0ull, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                              : epoch;
+      done = __builtin_amdgcn_ballot_w64(f == epoch);
+      if (wait && done == ~0ull) {
+        late = false;
+        break;
+      }
+      if (wait) __builtin_amdgcn_s_sleep(2);
+    }
+    if (wait && mine) __hip_atomic_exchange(flags + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      sh[0] = (int)(uint32_t)done;
+      sh[1] = (int)(uint32_t)(done >> 32);
+      sh[2] = late;
+    }
+  }
+  __syncthreads();
+  const uint64_t done = ((uint64_t)(uint32_t)sh[1] << 32) | (uint32_t)sh[0];
+  __syncthreads();   // sh may be written again by the next call
+  return done;
+}
+
+// The merger's half: out = sum_pi exp(lse_pi - M) o_pi / sum_pi exp(lse_pi -
+// M) over the np partitions, in partition order (deterministic whichever
+// partition merges); lse = -inf carries no weight.  The group's nc columns
+// (row col_row(c), head col_head(c)) are spread over the nthreads threads:
+// 32 / CH threads per column, each taking CH chunks of 4 consecutive dims.
+// Partitions are read KB = 32 / CH at a time, every load of a batch in
+// flight together, with a running maximum (the sums so far are rescaled
+// when a batch raises it).  With np <= KB (one batch) the partials of the
+// partitions already done when the merger arrives are requested before it
+// waits for the others, so that their loads overlap the wait and only the
+// late partitions' reads follow it.  Every thread of the workgroup calls
+// this (it synchronises); sh: three ints of LDS.
 // part_o [np][rcap][H][128], part_lse [np][rcap][H], out bf16 [rows][H][128].
 template <int CH, class ColRow, class ColHead>
-__device__ void splitk_merge(const float* part_o, const float* part_lse, uint16_t* out, int H,
-                             int rcap, int np, int nc, ColRow col_row, ColHead col_head, int tid,
-                             bool poisoned) {
+__device__ void splitk_merge(uint64_t* flags, uint64_t epoch, int* sh, const float* part_o,
+                             const float* part_lse, uint16_t* out, int H, int rcap, int np, int nc,
+                             ColRow col_row, ColHead col_head, int tid) {
   constexpr int L = 32 / CH;          // threads per column
   constexpr int KB = 32 / CH;         // partitions per batch: 32 loads of 16 bytes
   const int c = tid / L;
-  if (c >= nc) return;
+  const bool act = c < nc;
   const int d0 = (tid % L) * 4 * CH;
-  const size_t col = (size_t)col_row(c) * H + col_head(c);
+  const size_t col = act ? (size_t)col_row(c) * H + col_head(c) : 0;
   const size_t pstride = (size_t)rcap * H;
   f32x4 acc[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f, M = neg_inf();
-  for (int k0 = 0; k0 < np; k0 += KB) {
-    float lk[KB];
-    f32x4 v[KB][CH];
+  float lk[KB];
+  f32x4 v[KB][CH];
+  auto load = [&](int q, int k) {
+    // the log-sum-exps of several groups' columns share cache lines, which
+    // another merger on this CU may have brought into its L1 before this
+    // group's partition wrote its value: read them at L2
+    lk[q] = __hip_atomic_load(const_cast<float*>(part_lse) + (size_t)k * pstride + col,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float* po = part_o + ((size_t)k * pstride + col) * kDim + d0;
 #pragma unroll
-    for (int q = 0; q < KB; ++q) {
-      const int k = min(k0 + q, np - 1);   // past np: re-read the last one, weight 0
-      lk[q] = part_lse[(size_t)k * pstride + col];
-      const float* po = part_o + ((size_t)k * pstride + col) * kDim + d0;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) v[q][j] = *reinterpret_cast<const f32x4*>(po + 4 * j);
-    }
+    for (int j = 0; j < CH; ++j) v[q][j] = *reinterpret_cast<const f32x4*>(po + 4 * j);
+  };
+  auto fold = [&](int k0) {
     float mb = M;
 #pragma unroll
     for (int q = 0; q < KB; ++q)
@@ -145,6 +166,30 @@ __device__ void splitk_merge(const float* part_o, const float* part_lse, uint16_
 #pragma unroll
         for (int j = 0; j < CH; ++j) acc[j] += w * v[q][j];
       }
+    }
+  };
+  bool poisoned;
+  if (np <= KB) {
+    const uint64_t early = splitk_flags(flags, np, epoch, false, sh);
+#pragma unroll
+    for (int q = 0; q < KB; ++q)
+      if (act && q < np && ((early >> q) & 1ull)) load(q, q);
+    splitk_flags(flags, np, epoch, true, sh);
+    poisoned = sh[2] != 0;   // (read before any later write: the next call of
+                             //  splitk_flags is in another launch)
+    if (!act) return;
+#pragma unroll
+    for (int q = 0; q < KB; ++q)
+      if (q < np && !((early >> q) & 1ull)) load(q, q);
+    fold(0);
+  } else {
+    splitk_flags(flags, np, epoch, true, sh);
+    poisoned = sh[2] != 0;
+    if (!act) return;
+    for (int k0 = 0; k0 < np; k0 += KB) {
+#pragma unroll
+      for (int q = 0; q < KB; ++q) load(q, min(k0 + q, np - 1));   // past np: re-read the last one, weight 0
+      fold(k0);
     }
   }
   const float dinv = poisoned ? __builtin_nanf("") : den > 0.f ? 1.f / den : 0.f;
