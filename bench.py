@@ -295,6 +295,55 @@ def kernel_source_hash(workload="decode_batch64"):
 FLUSH_BYTES = 512 * 2**20   # more than L2 (8 x 4 MB) plus the 256 MB last-level cache
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence.
+    A default event (torch.cuda.Event) releases to system scope when it is
+    recorded, which writes back and invalidates the GPU caches between the
+    calls it brackets: time that the calls never spend inside a step, and a
+    cache state they never meet there.  The functions come from the HIP
+    runtime the process has already loaded (torch's, which libmsa shares)."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        import ctypes
+        rc = self._lib().hipEventRecord(self._ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._ev:
+            self._hip.hipEventDestroy(self._ev)
+
+
 def cold_call_ms(fn, stream, runs):
     """Median time of one call of `fn` on `stream` (HIP events around it),
     each run preceded, outside the events, by a read of a 512 MiB scratch
@@ -312,8 +361,7 @@ def cold_call_ms(fn, stream, runs):
     times = []
     for i in range(runs):
         scratch.sum()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         fn()
         b.record(stream)
@@ -522,12 +570,13 @@ def run(workload, args):
     gpu_step_ms = t_start.elapsed_time(t_end) / K
 
     # Per-call averages in the step's own context: K more steps after the
-    # timed region, with HIP events around each call on the launch stream
-    # (kept out of the timed region, where they would add gaps).  Repeating
-    # one call alone would let its data stay in the 256 MB last-level cache
-    # (the FP8 128k attention reads 268 MB), which never happens within a
-    # step, where the other call's reads evict it.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # timed region, with timing-only HIP events (no cache write-back at
+    # record) around each call on the launch stream (kept out of the timed
+    # region, where they would add gaps).  Repeating one call alone would let
+    # its data stay in the 256 MB last-level cache (the FP8 128k attention
+    # reads 268 MB), which never happens within a step, where the other
+    # call's reads evict it.
+    ev = [[TimingEvent() for _ in range(3)] for _ in range(K)]
     for e in ev:
         e[0].record(stream)
         indexer()
@@ -537,16 +586,6 @@ def run(workload, args):
     torch.cuda.synchronize()
     idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     att_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-
-    def per_call_ms(fn):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(K):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / K
 
     cold = {"indexer_call": cold_call_ms(indexer, stream, args.cold_runs),
             "attention_call": cold_call_ms(attention, stream, args.cold_runs),
